@@ -1,0 +1,124 @@
+// Shared device helpers of the MoE-layer HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+#define MOE_WAVE 64
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Scalar format conversions (16-bit storage as uint16_t)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// float32 -> bfloat16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t b) {
+  _Float16 h;
+  __builtin_memcpy(&h, &b, 2);
+  return (float)h;
+}
+
+// float32 -> binary16, round to nearest even (hardware conversion).
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  _Float16 h = (_Float16)f;
+  uint16_t b;
+  __builtin_memcpy(&b, &h, 2);
+  return b;
+}
+
+// OCP E4M3FN code -> float32.  Normal codes: the 7 magnitude bits placed at
+// the top of a binary32 exponent/mantissa field give 1.m * 2^(e-127); scaling
+// by 2^120 moves the exponent bias from 127 to 7.  Subnormal codes (exponent
+// field 0) are m * 2^-9.  NaN codes are never produced by the weight encoder.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  uint32_t mag = code & 0x7fu;
+  float v = (mag >= 8u) ? __uint_as_float((mag << 20) + (120u << 23))
+                        : (float)mag * 0.001953125f;
+  return (code & 0x80u) ? -v : v;
+}
+
+template <int DT> struct Act;
+template <> struct Act<MOE_DTYPE_F32> {
+  typedef float T;
+  static __device__ __forceinline__ float load(T v) { return v; }
+  static __device__ __forceinline__ T store(float f) { return f; }
+};
+template <> struct Act<MOE_DTYPE_F16> {
+  typedef uint16_t T;
+  static __device__ __forceinline__ float load(T v) { return f16_to_f32(v); }
+  static __device__ __forceinline__ T store(float f) { return f32_to_f16(f); }
+};
+template <> struct Act<MOE_DTYPE_BF16> {
+  typedef uint16_t T;
+  static __device__ __forceinline__ float load(T v) { return bf16_to_f32(v); }
+  static __device__ __forceinline__ T store(float f) { return f32_to_bf16(f); }
+};
+
+// 16 bytes of a 16-bit activation row -> 8 floats.
+template <int DT>
+__device__ __forceinline__ void unpack8(const uint4& q, float* f) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = Act<DT>::load((uint16_t)(w[i] & 0xffffu));
+    f[2 * i + 1] = Act<DT>::load((uint16_t)(w[i] >> 16));
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ uint4 pack8(const float* f) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = (uint32_t)Act<DT>::store(f[2 * i]) |
+           ((uint32_t)Act<DT>::store(f[2 * i + 1]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// ---------------------------------------------------------------------------
+// Wave primitives
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint64_t w = __shfl_xor(v, o, MOE_WAVE);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (MOE_WAVE - 1); }
+
+}  // namespace moe
+
+// Host-side launch check used by the entry points.
+#define MOE_LAUNCH_CHECK()                                   \
+  do {                                                       \
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)

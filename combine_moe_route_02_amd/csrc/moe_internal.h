@@ -1,0 +1,42 @@
+// Host-side launchers shared between the translation units of the library.
+#pragma once
+
+#include "moe_common.h"
+
+namespace moe {
+
+enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_GELU = 2, EPI_F32 = 3 };
+
+// One grouped GEMM  C[r, n] = epi( sum_k A[r, k] * B_g[n', k] )  over the
+// row segments of groups g = 0..n_groups-1.
+struct GemmArgs {
+  const void* A;          // activations, 16-bit or f32
+  long long lda;
+  const void* B;          // weights of group 0; group g at B + g * strideB
+  long long strideB;      // elements (bytes for fp8)
+  long long ldb;
+  const float* Bscale;    // fp8: [G][rows/128][K/128]
+  long long strideS;
+  void* C;
+  long long ldc;
+  const int32_t* offsets; // device: rows of group g = [offsets[e_begin+g], offsets[e_begin+g+1])
+  int e_begin;
+  int n_groups;
+  int dense_M;            // offsets == nullptr: one group of dense_M rows
+  int a_local;            // A row index = r - offsets[e_begin] (else r)
+  int c_local;            // C row index = r - offsets[e_begin] (else r)
+  int a_rows;             // a_local: rows of A (reads are clamped below it)
+  int c_rows;             // c_local: rows of C (rows at or past it are not written)
+  int Nb;                 // weight rows used by the tile grid (2I for SwiGLU)
+  int I;                  // SwiGLU split: gate rows [0, I), up rows [I, 2I)
+  int K;
+  int mt_slots;           // m-tile slots in the grid
+  int n_tiles;
+  int gm;                 // m-tiles per band in the tile order
+};
+
+// GEMM launchers; return MOE_OK / MOE_ERR_UNSUPPORTED / MOE_ERR_HIP.
+int launch_grouped_gemm(int act_dtype, int w_dtype, int epi, GemmArgs a,
+                        int max_rows, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,232 @@
+// Router scores and top-k gating.
+//
+// A router scores each token against every expert and the top-k experts are
+// kept (ThunderEP page, section 1.1; GPT-4 MoE page, section 2.3 stage 1).
+// Gate weights are either the softmax over all experts, evaluated at the
+// picks, with an optional temperature (GPT-4 MoE page, section 4.1 step 2;
+// xDeepServe diary, section 5.3), or a sigmoid of each picked score, and
+// may be renormalised to sum 1.
+//
+// Selection key.  s = logit + bias (one float32 add), -0.0 made +0.0, mapped
+// to an order-preserving uint32 and placed above the complement of the
+// expert index: the largest 64-bit key is the largest score and, among equal
+// scores, the lowest index.  One wave owns a token; k rounds of a wave-wide
+// uint64 max pick the experts in descending order.
+
+#include "moe_internal.h"
+
+namespace moe {
+
+__device__ __forceinline__ uint64_t select_key(float s, int e) {
+  if (s == 0.0f) s = 0.0f;  // -0.0 ties with +0.0
+  const uint32_t b = __float_as_uint(s);
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint32_t)(~(uint32_t)e);
+}
+
+__device__ __forceinline__ float key_score(uint64_t key) {
+  const uint32_t ord = (uint32_t)(key >> 32);
+  const uint32_t b = (ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord;
+  return __uint_as_float(b);
+}
+
+// One wave per token; EPL = experts per lane (lane l holds e = l + 64*i).
+template <int EPL>
+__global__ void __launch_bounds__(256)
+    topk_gate_kernel(const float* __restrict__ logits, const float* __restrict__ bias,
+                     int T, int E, int k, int gate, int renorm, float inv_temp,
+                     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  const int lane = lane_id();
+  const int t = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
+  if (t >= T) return;
+  const float* lg = logits + (long long)t * E;
+  float s[EPL];
+  uint64_t key[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) {
+      float v = lg[e];
+      if (bias) v = v + bias[e];
+      s[i] = v;
+      key[i] = select_key(v, e);
+    } else {
+      s[i] = 0.0f;
+      key[i] = 0;  // below every real key
+    }
+  }
+  uint64_t mine = 0;  // lane j keeps the j-th pick
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (key[i] == best) key[i] = 0;
+    if (lane == j) mine = best;
+  }
+  const uint64_t top = __shfl(mine, 0, MOE_WAVE);
+  const float smax = key_score(top);
+  float w = 0.0f;
+  const float sj = key_score(mine);
+  if (gate == MOE_GATE_SOFTMAX) {
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (lane + 64 * i < E) part += expf((s[i] - smax) * inv_temp);
+    const float denom = wave_sum(part);
+    w = expf((sj - smax) * inv_temp) / denom;
+  } else {
+    w = 1.0f / (1.0f + expf(-sj));
+  }
+  if (renorm) {
+    const float tot = wave_sum(lane < k ? w : 0.0f);
+    w = w / tot;
+  }
+  if (lane < k) {
+    topk_idx[(long long)t * k + lane] = (int32_t)(~(uint32_t)mine);
+    topk_w[(long long)t * k + lane] = w;
+  }
+}
+
+// 8 consecutive activations -> float (one or two 16-byte loads).
+template <int DT>
+__device__ __forceinline__ void load8(const typename Act<DT>::T* p, float* f) {
+  if (DT == MOE_DTYPE_F32) {
+    const float4 a = *(const float4*)p, b = *(const float4*)((const float*)p + 4);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  } else {
+    unpack8<DT>(*(const uint4*)p, f);
+  }
+}
+
+// Router projection for a few experts: one wave handles TPW tokens, lanes
+// stride over H in 8-element chunks, E <= EMAX accumulators per token.
+template <int DT, int TPW, int EMAX>
+__global__ void __launch_bounds__(256)
+    router_valu_kernel(const void* __restrict__ x, const void* __restrict__ wr, int T,
+                       int H, int E, float* __restrict__ logits) {
+  typedef typename Act<DT>::T ST;
+  const int lane = lane_id();
+  const int wave = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
+  const int t0 = wave * TPW;
+  if (t0 >= T) return;
+  float acc[TPW][EMAX];
+#pragma unroll
+  for (int a = 0; a < TPW; ++a)
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) acc[a][e] = 0.0f;
+  const ST* X = (const ST*)x;
+  const ST* W = (const ST*)wr;
+  const int nch = H >> 3;
+  for (int c = lane; c < nch; c += 64) {
+    float xf[TPW][8];
+#pragma unroll
+    for (int a = 0; a < TPW; ++a) {
+      const int t = min(t0 + a, T - 1);
+      load8<DT>(X + (long long)t * H + c * 8, xf[a]);
+    }
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      if (e < E) {
+        float wf[8];
+        load8<DT>(W + (long long)e * H + c * 8, wf);
+#pragma unroll
+        for (int a = 0; a < TPW; ++a)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[a][e] = fmaf(xf[a][q], wf[q], acc[a][e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < TPW; ++a) {
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      if (e < E) {
+        const float v = wave_sum(acc[a][e]);
+        if (lane == 0 && t0 + a < T) logits[(long long)(t0 + a) * E + e] = v;
+      }
+    }
+  }
+}
+
+namespace {
+
+template <int DT>
+int launch_router_valu(const void* x, const void* wr, int T, int H, int E,
+                       float* logits, hipStream_t s) {
+  const int waves_per_block = 4;
+  if (E <= 16) {
+    constexpr int TPW = 4;
+    const int waves = (T + TPW - 1) / TPW;
+    hipLaunchKernelGGL((router_valu_kernel<DT, TPW, 16>),
+                       dim3((waves + waves_per_block - 1) / waves_per_block),
+                       dim3(256), 0, s, x, wr, T, H, E, logits);
+  } else if (E <= 128) {
+    const int waves = T;
+    hipLaunchKernelGGL((router_valu_kernel<DT, 1, 128>),
+                       dim3((waves + waves_per_block - 1) / waves_per_block),
+                       dim3(256), 0, s, x, wr, T, H, E, logits);
+  } else {
+    return MOE_ERR_UNSUPPORTED;
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int launch_topk(const float* logits, const float* bias, int T, int E, int k,
+                int gate, int renorm, float inv_temp, int32_t* idx, float* w,
+                hipStream_t s) {
+  const dim3 grid((T + 3) / 4), block(256);
+#define MOE_TOPK(EPL)                                                         \
+  hipLaunchKernelGGL((topk_gate_kernel<EPL>), grid, block, 0, s, logits, bias, \
+                     T, E, k, gate, renorm, inv_temp, idx, w)
+  if (E <= 64) MOE_TOPK(1);
+  else if (E <= 128) MOE_TOPK(2);
+  else if (E <= 256) MOE_TOPK(4);
+  else if (E <= 512) MOE_TOPK(8);
+  else MOE_TOPK(16);
+#undef MOE_TOPK
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace
+
+int route_impl(const void* x, const void* w_router, int act_dtype, const float* bias,
+               int T, int H, int E, int k, int gate, int renorm, float inv_temp,
+               float* logits, int32_t* topk_idx, float* topk_w, hipStream_t s) {
+  if (T == 0) return MOE_OK;
+  if (w_router) {
+    int st;
+    const bool mfma = act_dtype != MOE_DTYPE_F32 && E >= 128 && E % 128 == 0 &&
+                      H % 64 == 0;
+    if (mfma) {
+      GemmArgs a{};
+      a.A = x;
+      a.lda = H;
+      a.B = w_router;
+      a.strideB = 0;
+      a.ldb = H;
+      a.C = logits;
+      a.ldc = E;
+      a.offsets = nullptr;
+      a.n_groups = 1;
+      a.dense_M = T;
+      a.Nb = E;
+      a.I = 0;
+      a.K = H;
+      st = launch_grouped_gemm(act_dtype, act_dtype, EPI_F32, a, T, s);
+    } else if (act_dtype == MOE_DTYPE_F32) {
+      st = launch_router_valu<MOE_DTYPE_F32>(x, w_router, T, H, E, logits, s);
+    } else if (act_dtype == MOE_DTYPE_F16) {
+      st = launch_router_valu<MOE_DTYPE_F16>(x, w_router, T, H, E, logits, s);
+    } else {
+      st = launch_router_valu<MOE_DTYPE_BF16>(x, w_router, T, H, E, logits, s);
+    }
+    if (st != MOE_OK) return st;
+  }
+  return launch_topk(logits, bias, T, E, k, gate, renorm, inv_temp, topk_idx, topk_w, s);
+}
+
+}  // namespace moe

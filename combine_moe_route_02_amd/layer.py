@@ -1,0 +1,134 @@
+"""A MoE layer forward on one GPU driven through the C ABI.
+
+Buffers are torch tensors (device memory and streams only); each step is one
+call into libmoe.so: route -> dispatch -> expert FFN -> combine, or the fused
+kernel after route and dispatch.  Nothing here computes any part of the
+layer.
+"""
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+GATES = {"softmax": L.GATE_SOFTMAX, "sigmoid": L.GATE_SIGMOID}
+ACTS = {"swiglu": L.ACT_SWIGLU, "gelu": L.ACT_GELU}
+
+
+@dataclass(frozen=True)
+class LayerSpec:
+    T: int
+    H: int
+    E: int
+    k: int
+    I: int
+    act_dtype: torch.dtype
+    gate: str = "softmax"
+    renorm: bool = False
+    act: str = "swiglu"
+    e_begin: int = 0
+    e_end: int = -1          # -1: all experts are local
+    inv_temperature: float = 1.0
+
+    @property
+    def local(self):
+        return self.e_begin, (self.E if self.e_end < 0 else self.e_end)
+
+    @property
+    def max_rows(self) -> int:
+        e0, e1 = self.local
+        return self.T * min(self.k, e1 - e0)
+
+
+class MoELayer:
+    """Owns the per-call buffers of one layer shape on one device."""
+
+    def __init__(self, spec: LayerSpec, device="cuda"):
+        s = self.spec = spec
+        dev = torch.device(device)
+        N = s.T * s.k
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.logits = torch.empty((s.T, s.E), dtype=torch.float32, device=dev)
+        self.topk_idx = torch.empty((s.T, s.k), **i32)
+        self.topk_w = torch.empty((s.T, s.k), dtype=torch.float32, device=dev)
+        self.counts = torch.empty((s.E,), **i32)
+        self.offsets = torch.empty((s.E + 1,), **i32)
+        self.slot_of = torch.empty((s.T, s.k), **i32)
+        self.row_token = torch.empty((N,), **i32)
+        self.x_perm = torch.empty((N, s.H), dtype=s.act_dtype, device=dev)
+        self.h = torch.empty((max(s.max_rows, 1), s.I), dtype=s.act_dtype, device=dev)
+        self.y_perm = torch.zeros((N, s.H), dtype=s.act_dtype, device=dev)
+        self.out = torch.empty((s.T, s.H), dtype=s.act_dtype, device=dev)
+        nb = L.moe_workspace_bytes(L.WS_DISPATCH, s.T, s.H, s.E, s.k, s.I)
+        self.ws = torch.empty((max(nb, 16),), dtype=torch.uint8, device=dev)
+        self.ws_fused = None
+
+    # -- the four calls -----------------------------------------------------
+    def route(self, x, w_router, bias=None, stream=None):
+        s = self.spec
+        L.moe_route(x, w_router, bias, s.k, GATES[s.gate], s.renorm, s.inv_temperature,
+                    self.logits, self.topk_idx, self.topk_w, stream=stream)
+
+    def route_from_logits(self, bias=None, stream=None):
+        """Top-k gating on the scores already in self.logits."""
+        s = self.spec
+        L.moe_route(None, None, bias, s.k, GATES[s.gate], s.renorm, s.inv_temperature,
+                    self.logits, self.topk_idx, self.topk_w,
+                    act_dtype=L.DTYPE_OF[s.act_dtype], stream=stream)
+
+    def dispatch(self, x, stream=None):
+        s = self.spec
+        e0, e1 = s.local
+        L.moe_dispatch(x, self.topk_idx, s.E, e0, e1, self.counts, self.offsets,
+                       self.slot_of, self.row_token, self.x_perm, self.ws, stream=stream)
+
+    def ffn_up(self, w13, w13_scale=None, stream=None):
+        s = self.spec
+        e0, e1 = s.local
+        L.moe_expert_ffn_up(self.x_perm, self.offsets, s.H, s.I, e0, e1, s.max_rows,
+                            ACTS[s.act], w13, w13_scale, self.h, stream=stream)
+
+    def ffn_down(self, w2, w2_scale=None, stream=None):
+        s = self.spec
+        e0, e1 = s.local
+        L.moe_expert_ffn_down(self.offsets, s.H, s.I, e0, e1, s.max_rows, w2, w2_scale,
+                              self.h, self.y_perm, stream=stream)
+
+    def ffn(self, w13, w2, w13_scale=None, w2_scale=None, stream=None):
+        s = self.spec
+        e0, e1 = s.local
+        L.moe_expert_ffn(self.x_perm, self.offsets, s.H, s.I, e0, e1, s.max_rows,
+                         ACTS[s.act], w13, w13_scale, w2, w2_scale, self.h, self.y_perm,
+                         stream=stream)
+
+    def combine(self, stream=None):
+        L.moe_combine(self.y_perm, self.slot_of, self.topk_w, self.out, stream=stream)
+
+    def forward(self, x, w_router, bias, w13, w2, w13_scale=None, w2_scale=None,
+                stream=None) -> torch.Tensor:
+        self.route(x, w_router, bias, stream)
+        self.dispatch(x, stream)
+        self.ffn_up(w13, w13_scale, stream)
+        self.ffn_down(w2, w2_scale, stream)
+        self.combine(stream)
+        return self.out
+
+    # -- fused variant ------------------------------------------------------
+    def fused(self, x, w13, w2, stream=None):
+        s = self.spec
+        e0, e1 = s.local
+        if self.ws_fused is None:
+            nb = L.moe_workspace_bytes(L.WS_FUSED, s.T, s.H, s.E, s.k, s.I)
+            self.ws_fused = torch.empty((max(nb, 16),), dtype=torch.uint8,
+                                        device=self.out.device)
+        L.moe_layer_fused(x, self.offsets, self.slot_of, self.row_token, self.topk_w,
+                          s.E, s.I, e0, e1, ACTS[s.act], w13, w2, self.h, self.y_perm,
+                          self.out, self.ws_fused, stream=stream)
+
+    def forward_fused(self, x, w_router, bias, w13, w2, stream=None) -> torch.Tensor:
+        self.route(x, w_router, bias, stream)
+        self.dispatch(x, stream)   # counts/offsets/layout; its gather is unused here
+        self.fused(x, w13, w2, stream)
+        return self.out

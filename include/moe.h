@@ -1,0 +1,218 @@
+/*
+ * moe.h - C ABI of the MoE expert-parallel layer forward on one MI355X.
+ *
+ * The layer is the pages' statement of the problem, run on one GPU's share:
+ *   moe_route      router scores and top-k gating
+ *   moe_dispatch   per-expert counts, offsets, the token <-> slot layout map
+ *                  and the permute-gather into expert-contiguous rows
+ *   moe_expert_ffn grouped expert FFN (GEMM-1 + activation, GEMM-2)
+ *   moe_combine    gate-weighted sum of each token's k expert outputs
+ * plus moe_layer_fused, which runs gather -> GEMM-1 -> GEMM-2 -> combine as
+ * one persistent, token-tile-pipelined kernel.
+ *
+ * Conventions (all calls):
+ *  - Every pointer is a device pointer unless stated otherwise; the caller
+ *    owns every buffer.  The library never allocates or frees memory, never
+ *    copies device data to the host and never synchronises: all work is
+ *    enqueued on `stream` (0 = the null stream) and the calls can be captured
+ *    in a hipGraph.  Sizes that depend on the routing (per-expert counts) are
+ *    read on the device, never by the host (TensorRT-LLM large-EP page,
+ *    "EP communication kernels": sizes read from GPU memory so that the step
+ *    stays graph-capturable).
+ *  - Arguments are validated on the host before anything is launched; a
+ *    negative return code means nothing was enqueued.  MOE_ERR_HIP means a
+ *    launch failed (hipGetLastError).  Faults inside kernels are not reported
+ *    synchronously.
+ *  - Index type is int32; calls with T*k >= 2^31 are rejected.
+ *  - Rows are contiguous with leading dimension H (or I); x, x_perm, y_perm,
+ *    out and the weights must be 16-byte aligned.  Logits must be finite.
+ *  - act_dtype selects the activation format: MOE_DTYPE_F32, MOE_DTYPE_F16
+ *    or MOE_DTYPE_BF16.  Expert weights use act_dtype, or MOE_DTYPE_FP8_E4M3
+ *    (OCP E4M3FN codes with one float32 scale per 128x128 tile) with bf16
+ *    activations.
+ *  - Calls are stateless and re-entrant.
+ */
+#ifndef MOE_ROUTE_MI355X_H
+#define MOE_ROUTE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_ARG = -1,          /* null pointer, bad size or range            */
+  MOE_ERR_UNSUPPORTED = -2,  /* valid but not implemented (dtype, shape)   */
+  MOE_ERR_WORKSPACE = -3,    /* workspace missing or too small             */
+  MOE_ERR_HIP = -4           /* a kernel launch failed                     */
+};
+
+enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_F16 = 1, MOE_DTYPE_BF16 = 2,
+                 MOE_DTYPE_FP8_E4M3 = 3 };
+enum moe_gate { MOE_GATE_SOFTMAX = 0, MOE_GATE_SIGMOID = 1 };
+enum moe_act { MOE_ACT_SWIGLU = 0, MOE_ACT_GELU = 1 };
+enum moe_ws_kind { MOE_WS_DISPATCH = 0, MOE_WS_FFN = 1, MOE_WS_FUSED = 2 };
+
+/*
+ * moe_route - router logits and top-k gating for T tokens.
+ *
+ * Defines: a router gives every token one score per expert and the top-k
+ * experts are chosen (ThunderEP page, section 1.1); softmax over all experts
+ * with an optional temperature, then top-k, the weights being the selected
+ * probabilities (GPT-4 MoE page, section 4.1, step 2; temperature default
+ * 1.0 in the xDeepServe diary, section 5.3).
+ *
+ *  x         [T][H] act_dtype activations.
+ *  w_router  [E][H] act_dtype router weights, or NULL.  When given, the
+ *            call first computes logits[t][e] = sum_h x[t][h]*w_router[e][h]
+ *            (float32 accumulation) into `logits`; when NULL, `logits` is an
+ *            input and x is not read.
+ *  bias      [E] float32 added to the logits before selection, or NULL.
+ *  gate      MOE_GATE_SOFTMAX: w = softmax over all E of (s * inv_temperature)
+ *            evaluated at the picks; MOE_GATE_SIGMOID: w = 1/(1+exp(-s)).
+ *            s = logits + bias (one float32 addition).
+ *  renorm    nonzero: the k weights of a token are divided by their sum.
+ *  logits    [T][E] float32 (output, or input when w_router is NULL).
+ *  topk_idx  [T][k] int32 output: experts by descending s, ties to the lower
+ *            index (-0.0 ties with +0.0).
+ *  topk_w    [T][k] float32 output: gate weights in the same order.
+ * Limits: 1 <= k <= E <= 1024, k <= 32, H % 8 == 0.
+ */
+int moe_route(const void* x, const void* w_router, int act_dtype,
+              const float* bias, int T, int H, int E, int k, int gate,
+              int renorm, float inv_temperature, float* logits,
+              int32_t* topk_idx, float* topk_w, hipStream_t stream);
+
+/*
+ * moe_dispatch - counts, offsets, layout map and permute-gather.
+ *
+ * Defines: dispatch sends each token once to every one of its k experts
+ * (DySHARP page, section 1); the destination keeps an algebraic -> layout
+ * index table that packs arriving tokens densely, reused in reverse by
+ * combine (DySHARP page, section 3.1, item 3); tokens bound for one expert
+ * are gathered into one contiguous buffer (ThunderEP page, sections 3.4 and
+ * 5.2).
+ *
+ *  x          [T][H] act_dtype.
+ *  topk_idx   [T][k] int32, each in [0, E), distinct within a token.
+ *  counts     [E]   int32 output: (token, pick) pairs per expert.
+ *  offsets    [E+1] int32 output: exclusive prefix sum, offsets[E] = T*k.
+ *  slot_of    [T][k] int32 output: layout row of pick j of token t
+ *             = offsets[e] + (number of earlier tokens that picked e).
+ *  row_token  [T*k] int32 output: inverse of slot_of (token of each row).
+ *  x_perm     [T*k][H] act_dtype output: x_perm[r] = x[row_token[r]] for the
+ *             rows of local experts e_begin <= e < e_end only (global row
+ *             numbering; other rows are not written).
+ *  ws         workspace of at least moe_workspace_bytes(MOE_WS_DISPATCH, ...)
+ *             bytes (per-tile histograms); contents need not be initialised.
+ * Counts, offsets and the layout map cover all E experts.
+ */
+int moe_dispatch(const void* x, int act_dtype, const int32_t* topk_idx,
+                 int T, int H, int E, int k, int e_begin, int e_end,
+                 int32_t* counts, int32_t* offsets, int32_t* slot_of,
+                 int32_t* row_token, void* x_perm, void* ws, size_t ws_bytes,
+                 hipStream_t stream);
+
+/*
+ * moe_expert_ffn - grouped expert FFN over the local experts' rows.
+ *
+ * Defines: each expert is an FFN, Linear -> activation -> Linear (GPT-4 MoE
+ * page, section 3.1 table); the gated SwiGLU form uses two first-layer
+ * projections.  Expert e (local index g = e - e_begin) owns rows
+ * [offsets[e], offsets[e+1]) of x_perm; offsets are read on the device.
+ *
+ *  x_perm     [*][H] act_dtype, global row numbering (as moe_dispatch).
+ *  w13        act MOE_ACT_SWIGLU: [E_loc][2I][H]; rows [0,I) are the gate
+ *             projection and rows [I,2I) the up projection.
+ *             act MOE_ACT_GELU: [E_loc][I][H].
+ *  w2         [E_loc][H][I].
+ *  w13_scale, w2_scale  float32 scales, one per 128x128 tile
+ *             ([E_loc][rows/128][cols/128]) when w_dtype is FP8_E4M3, else
+ *             NULL.
+ *  h_ws       [max_rows][I] act_dtype workspace for the activation; row
+ *             r - offsets[e_begin].
+ *  y_perm     [*][H] act_dtype output, global row numbering; only local rows
+ *             are written, so rows of other experts keep what the caller put
+ *             there (outputs received from other GPUs).
+ *  max_rows   host bound on offsets[e_end] - offsets[e_begin], typically
+ *             T*min(k, E_loc); it sizes the grid.
+ * Computation: fp32 accumulation; SwiGLU h = silu(x Wg^T) * (x Wu^T), GELU
+ * h = gelu_erf(x W1^T), h rounded once to act_dtype; y = h W2^T rounded once.
+ * Limits: H % 256 == 0 and I % 128 == 0 for 16-bit types; fp32 needs
+ * H % 64 == 0 and I % 64 == 0; ws may be NULL (no workspace used).
+ */
+int moe_expert_ffn(const void* x_perm, const int32_t* offsets, int act_dtype,
+                   int H, int I, int e_begin, int e_end, int max_rows, int act,
+                   const void* w13, const float* w13_scale, const void* w2,
+                   const float* w2_scale, int w_dtype, void* h_ws,
+                   void* y_perm, void* ws, size_t ws_bytes,
+                   hipStream_t stream);
+
+/* The two halves of moe_expert_ffn, same arguments and rules:
+ * _up computes h from x_perm (GEMM-1 + activation), _down computes y_perm
+ * from h (GEMM-2).  moe_expert_ffn = _up then _down on the same stream. */
+int moe_expert_ffn_up(const void* x_perm, const int32_t* offsets,
+                      int act_dtype, int H, int I, int e_begin, int e_end,
+                      int max_rows, int act, const void* w13,
+                      const float* w13_scale, int w_dtype, void* h_ws,
+                      hipStream_t stream);
+int moe_expert_ffn_down(const int32_t* offsets, int act_dtype, int H, int I,
+                        int e_begin, int e_end, int max_rows, const void* w2,
+                        const float* w2_scale, int w_dtype, const void* h_ws,
+                        void* y_perm, hipStream_t stream);
+
+/*
+ * moe_combine - gate-weighted un-permute reduction.
+ *
+ * Defines: combine brings the k expert results of a token back to it and
+ * reduces them into one (DySHARP page, section 1), as a weighted sum
+ * (ThunderEP page, section 2.1).
+ *
+ *  y_perm  [T*k][H] act_dtype (global row numbering).
+ *  slot_of [T][k] int32, topk_w [T][k] float32 (from dispatch / route).
+ *  out     [T][H] act_dtype: out[t] = sum_j topk_w[t][j] * y_perm[slot_of[t][j]],
+ *          accumulated in float32 in pick order and rounded once.
+ */
+int moe_combine(const void* y_perm, const int32_t* slot_of,
+                const float* topk_w, int act_dtype, int T, int H, int k,
+                void* out, hipStream_t stream);
+
+/*
+ * moe_layer_fused - gather -> GEMM-1 -> GEMM-2 -> combine in one persistent
+ * kernel, pipelined at 128-row token tiles.
+ *
+ * Defines: the token-centric fusion of dispatch, both expert GEMMs and
+ * combine, with readiness gating per tile and a combine that fires once a
+ * token's expert outputs are complete (DySHARP page, section 3.2).
+ *
+ * Inputs are those of moe_dispatch/moe_expert_ffn/moe_combine after
+ * moe_route and moe_dispatch have produced offsets, slot_of and row_token
+ * (x_perm is not needed: GEMM-1 gathers its rows from x via row_token).
+ * Results equal moe_expert_ffn followed by moe_combine: h_ws, y_perm (local
+ * rows) and out are written.  ws must hold
+ * moe_workspace_bytes(MOE_WS_FUSED, ...) bytes; it is initialised by the
+ * call.  Supported for 16-bit activations with 16-bit weights.
+ */
+int moe_layer_fused(const void* x, const int32_t* offsets,
+                    const int32_t* slot_of, const int32_t* row_token,
+                    const float* topk_w, int act_dtype, int T, int H, int E,
+                    int k, int I, int e_begin, int e_end, int act,
+                    const void* w13, const void* w2, void* h_ws, void* y_perm,
+                    void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes needed by moe_dispatch (MOE_WS_DISPATCH), moe_expert_ffn
+ * (MOE_WS_FFN; 0) or moe_layer_fused (MOE_WS_FUSED) for these sizes. */
+size_t moe_workspace_bytes(int which, int T, int H, int E, int k, int I);
+
+/* Static, human-readable text for a status code. */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTE_MI355X_H */

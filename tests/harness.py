@@ -1,0 +1,129 @@
+"""Helpers shared by the GPU parity tests: run the HIP layer, run the oracle on
+the same input bytes, compare.
+
+Bars: bit-exact for indices, counts, offsets, the layout map and x_perm;
+rel-L2 <= 1e-5 for float32 results (logits, gate weights, the fp32 layer);
+rel-L2 <= 1e-2 for bf16 / fp16 / fp8-weight results.
+"""
+
+import sys
+
+import numpy as np
+import torch
+
+from gen.configs import F32, LayerConfig
+from gen.inputs import TORCH_DTYPE, make_inputs
+from oracle import moe_oracle as O
+from oracle.torch_io import stored
+
+TOL_F32 = 1e-5
+TOL_16 = 1e-2
+
+
+def tol(cfg: LayerConfig) -> float:
+    return TOL_F32 if cfg.act_dtype == F32 else TOL_16
+
+
+def rel_l2(got, ref) -> float:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref)
+    num = np.linalg.norm(got - ref)
+    return float(num / den) if den > 0 else float(num)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def params(cfg: LayerConfig) -> O.LayerParams:
+    return O.LayerParams(T=cfg.T, H=cfg.H, E=cfg.E, k=cfg.k, I=cfg.I,
+                         act_dtype=cfg.act_dtype, w_dtype=cfg.w_dtype, gate=cfg.gate,
+                         renorm=cfg.renorm, act=cfg.act, e_begin=cfg.e_begin,
+                         e_end=cfg.e_end, inv_temperature=cfg.inv_temperature)
+
+
+def spec(cfg: LayerConfig):
+    from combine_moe_route_02_amd import LayerSpec
+    return LayerSpec(T=cfg.T, H=cfg.H, E=cfg.E, k=cfg.k, I=cfg.I,
+                     act_dtype=TORCH_DTYPE[cfg.act_dtype], gate=cfg.gate,
+                     renorm=cfg.renorm, act=cfg.act, e_begin=cfg.e_begin,
+                     e_end=cfg.e_end, inv_temperature=cfg.inv_temperature)
+
+
+def gpu_layer(cfg: LayerConfig, inp, fused=False):
+    """Run the whole layer through the C ABI on cuda:0; returns the MoELayer."""
+    from combine_moe_route_02_amd import MoELayer
+    say(f"[gpu] layer {cfg.name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I} "
+        f"{cfg.act_dtype}/{cfg.w_dtype} local=[{cfg.e_begin},{cfg.e_end}) fused={fused}")
+    lay = MoELayer(spec(cfg), "cuda")
+    if inp.get("y_remote") is not None:
+        lay.y_perm.copy_(inp["y_remote"])
+    if fused:
+        lay.forward_fused(inp["x"], inp["w_router"], inp["bias"], inp["w13"], inp["w2"])
+    else:
+        lay.forward(inp["x"], inp["w_router"], inp["bias"], inp["w13"], inp["w2"],
+                    inp["w13_scale"], inp["w2_scale"])
+    torch.cuda.synchronize()
+    return lay
+
+
+def to_device(inp, device="cuda"):
+    return {k: (v.to(device) if v is not None else None) for k, v in inp.items()}
+
+
+def np_stored(inp):
+    return {k: (stored(v) if v is not None else None) for k, v in inp.items()}
+
+
+def check_routing(cfg, lay, st):
+    """Integer path, bit-exact, with the oracle run on the GPU's own logits."""
+    logits = lay.logits.cpu().numpy()
+    idx, w = O.route(logits, st["bias"], cfg.k, cfg.gate, cfg.renorm, cfg.inv_temperature)
+    g_idx = lay.topk_idx.cpu().numpy()
+    assert np.array_equal(g_idx, idx), "topk_idx differs"
+    assert rel_l2(lay.topk_w.cpu().numpy(), w) <= TOL_F32
+    counts = O.expert_counts(idx, cfg.E)
+    offsets = O.expert_offsets(counts)
+    assert np.array_equal(lay.counts.cpu().numpy(), counts)
+    assert np.array_equal(lay.offsets.cpu().numpy(), offsets)
+    slot_of, row_token = O.layout_map(idx, offsets)
+    assert np.array_equal(lay.slot_of.cpu().numpy(), slot_of)
+    assert np.array_equal(lay.row_token.cpu().numpy(), row_token)
+    r0, r1 = int(offsets[cfg.e_begin]), int(offsets[cfg.e_end])
+    xp = stored(lay.x_perm[r0:r1])
+    assert np.array_equal(xp, O.gather_rows(st["x"], row_token, r0, r1)), "x_perm differs"
+    return dict(logits=logits, idx=idx, w=w, counts=counts, offsets=offsets,
+                slot_of=slot_of, row_token=row_token)
+
+
+def flipped_tokens(cfg, gpu_logits, own_logits, bias):
+    """Tokens whose top-k differs between the oracle's own scores and the GPU's."""
+    a, _ = O.route(gpu_logits, bias, cfg.k, cfg.gate, cfg.renorm, cfg.inv_temperature)
+    b, _ = O.route(own_logits, bias, cfg.k, cfg.gate, cfg.renorm, cfg.inv_temperature)
+    return np.nonzero((a != b).any(axis=1))[0]
+
+
+def full_parity(cfg: LayerConfig, inp_cpu, lay):
+    """Element-by-element comparison of every output (small layers)."""
+    st = np_stored(inp_cpu)
+    r = check_routing(cfg, lay, st)
+    p = params(cfg)
+    own = O.router_logits(O.decode(st["x"], cfg.act_dtype),
+                          O.decode(st["w_router"], cfg.act_dtype))
+    assert rel_l2(r["logits"], own) <= TOL_F32
+    flips = flipped_tokens(cfg, r["logits"], own, st["bias"])
+    assert len(flips) <= max(1, cfg.T // 1000), f"top-k flips at {flips[:10]}"
+    ref = O.layer_forward(p, st["x"], st["w_router"], st["bias"], st["w13"], st["w2"],
+                          st["w13_scale"], st["w2_scale"], st["y_remote"],
+                          logits=r["logits"])
+    r0, r1 = int(r["offsets"][cfg.e_begin]), int(r["offsets"][cfg.e_end])
+    y = O.decode(stored(lay.y_perm), cfg.act_dtype)
+    if r1 > r0:
+        e_y = rel_l2(y[r0:r1], ref["y_perm"][r0:r1])
+        assert e_y <= tol(cfg), f"y_perm rel-L2 {e_y}"
+    out = O.decode(stored(lay.out), cfg.act_dtype)
+    e_o = rel_l2(out, ref["out"])
+    assert e_o <= tol(cfg), f"out rel-L2 {e_o}"
+    return dict(out_rel=e_o, flips=len(flips))

@@ -1,0 +1,139 @@
+"""The C ABI loads and exports what include/moe.h declares; host-side
+validation rejects bad arguments before any launch (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import combine_moe_route_02_amd as M
+from combine_moe_route_02_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary_calls():
+    names = declared_functions()
+    for n in ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
+              "moe_layer_fused", "moe_workspace_bytes", "moe_status_string"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert sorted(L.EXPORTS) == declared_functions()
+
+
+def test_status_strings():
+    lib = L.lib()
+    assert lib.moe_status_string(0) == b"ok"
+    for code in (-1, -2, -3, -4):
+        assert lib.moe_status_string(code) not in (b"ok", b"unknown status")
+
+
+def test_workspace_sizes():
+    lib = L.lib()
+    # two int32 tables [E][ceil(T/256)]
+    assert lib.moe_workspace_bytes(L.WS_DISPATCH, 16384, 7168, 256, 8, 2048) == 2 * 256 * 64 * 4
+    assert lib.moe_workspace_bytes(L.WS_DISPATCH, 1, 8, 8, 1, 8) == 2 * 8 * 1 * 4
+    assert lib.moe_workspace_bytes(L.WS_FFN, 4096, 4096, 8, 1, 14336) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def _route(**kw):
+    a = dict(x=FAKE, w=FAKE, dt=L.DTYPE_BF16, bias=None, T=4, H=64, E=8, k=2,
+             gate=0, renorm=0, invt=1.0, logits=FAKE, idx=FAKE, w_out=FAKE)
+    a.update(kw)
+    return L.lib().moe_route(a["x"], a["w"], a["dt"], a["bias"], a["T"], a["H"], a["E"],
+                             a["k"], a["gate"], a["renorm"], a["invt"], a["logits"],
+                             a["idx"], a["w_out"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=0), L.MOE_ERR_ARG), (dict(k=9), L.MOE_ERR_ARG), (dict(E=0), L.MOE_ERR_ARG),
+    (dict(E=2000, k=2), L.MOE_ERR_ARG), (dict(k=33, E=64), L.MOE_ERR_ARG),
+    (dict(T=-1), L.MOE_ERR_ARG), (dict(gate=7), L.MOE_ERR_ARG),
+    (dict(dt=L.DTYPE_FP8_E4M3), L.MOE_ERR_UNSUPPORTED), (dict(dt=9), L.MOE_ERR_UNSUPPORTED),
+    (dict(H=12), L.MOE_ERR_ARG), (dict(logits=None), L.MOE_ERR_ARG),
+    (dict(invt=float("nan")), L.MOE_ERR_ARG), (dict(invt=-1.0), L.MOE_ERR_ARG),
+    (dict(T=1 << 28, k=8), L.MOE_ERR_ARG),
+    (dict(E=200, k=2), L.MOE_ERR_UNSUPPORTED),
+])
+def test_route_validation(kw, code):
+    assert _route(**kw) == code
+
+
+def _dispatch(**kw):
+    a = dict(x=FAKE, dt=L.DTYPE_BF16, idx=FAKE, T=4, H=64, E=8, k=2, e0=0, e1=8,
+             counts=FAKE, offsets=FAKE, slot=FAKE, rt=FAKE, xp=FAKE, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return L.lib().moe_dispatch(a["x"], a["dt"], a["idx"], a["T"], a["H"], a["E"], a["k"],
+                                a["e0"], a["e1"], a["counts"], a["offsets"], a["slot"],
+                                a["rt"], a["xp"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(e1=9), L.MOE_ERR_ARG), (dict(e0=5, e1=4), L.MOE_ERR_ARG),
+    (dict(e0=-1), L.MOE_ERR_ARG), (dict(k=9), L.MOE_ERR_ARG),
+    (dict(H=4), L.MOE_ERR_ARG), (dict(counts=None), L.MOE_ERR_ARG),
+    (dict(xp=None), L.MOE_ERR_ARG), (dict(ws=None), L.MOE_ERR_WORKSPACE),
+    (dict(wsb=8), L.MOE_ERR_WORKSPACE), (dict(dt=L.DTYPE_FP8_E4M3), L.MOE_ERR_UNSUPPORTED),
+])
+def test_dispatch_validation(kw, code):
+    assert _dispatch(**kw) == code
+
+
+def test_ffn_validation():
+    lib = L.lib()
+    f = lib.moe_expert_ffn
+    # fp8 weights need bf16 activations
+    assert f(FAKE, FAKE, L.DTYPE_F16, 256, 128, 0, 8, 64, 0, FAKE, FAKE, FAKE, FAKE,
+             L.DTYPE_FP8_E4M3, FAKE, FAKE, None, 0, None) == L.MOE_ERR_UNSUPPORTED
+    # fp8 without scales
+    assert f(FAKE, FAKE, L.DTYPE_BF16, 256, 128, 0, 8, 64, 0, FAKE, None, FAKE, None,
+             L.DTYPE_FP8_E4M3, FAKE, FAKE, None, 0, None) == L.MOE_ERR_ARG
+    # shapes the MFMA tiles do not cover
+    assert f(FAKE, FAKE, L.DTYPE_BF16, 200, 128, 0, 8, 64, 0, FAKE, None, FAKE, None,
+             L.DTYPE_BF16, FAKE, FAKE, None, 0, None) == L.MOE_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, L.DTYPE_BF16, 256, 96, 0, 8, 64, 0, FAKE, None, FAKE, None,
+             L.DTYPE_BF16, FAKE, FAKE, None, 0, None) == L.MOE_ERR_UNSUPPORTED
+    # bad activation and range
+    assert f(FAKE, FAKE, L.DTYPE_BF16, 256, 128, 0, 8, 64, 5, FAKE, None, FAKE, None,
+             L.DTYPE_BF16, FAKE, FAKE, None, 0, None) == L.MOE_ERR_ARG
+    assert lib.moe_expert_ffn_up(FAKE, FAKE, L.DTYPE_BF16, 256, 128, 3, 2, 64, 0, FAKE,
+                                 None, L.DTYPE_BF16, FAKE, None) == L.MOE_ERR_ARG
+    # empty local range / no rows: nothing to do
+    assert lib.moe_expert_ffn_up(FAKE, FAKE, L.DTYPE_BF16, 256, 128, 3, 3, 64, 0, FAKE,
+                                 None, L.DTYPE_BF16, FAKE, None) == L.MOE_OK
+
+
+def test_combine_and_fused_validation():
+    lib = L.lib()
+    assert lib.moe_combine(FAKE, FAKE, FAKE, L.DTYPE_BF16, 4, 64, 0, FAKE, None) == L.MOE_ERR_ARG
+    assert lib.moe_combine(FAKE, FAKE, FAKE, L.DTYPE_BF16, 4, 4, 1, FAKE, None) == L.MOE_ERR_ARG
+    assert lib.moe_combine(None, FAKE, FAKE, L.DTYPE_BF16, 4, 64, 1, FAKE, None) == L.MOE_ERR_ARG
+    assert lib.moe_combine(FAKE, FAKE, FAKE, L.DTYPE_BF16, 0, 64, 1, FAKE, None) == L.MOE_OK
+    assert lib.moe_layer_fused(FAKE, FAKE, FAKE, FAKE, FAKE, L.DTYPE_F32, 4, 256, 8, 2, 128,
+                               0, 8, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                               None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_layer_fused(FAKE, FAKE, FAKE, FAKE, FAKE, L.DTYPE_BF16, 4, 256, 8, 2, 128,
+                               0, 8, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                               None) == L.MOE_ERR_WORKSPACE
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", "/nonexistent/libmoe.so")
+    with pytest.raises(ImportError):
+        L.lib()

@@ -1,0 +1,126 @@
+"""GPU parity on small shapes: every output element against the oracle.
+
+The shapes span several MFMA tiles with ragged tails, and the edge cases of
+the method: one expert, k = E, all tokens on one expert, empty experts, no
+local expert, a single token, no tokens, mass ties in the scores, and both
+router paths (VALU for few experts, MFMA for many).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gen.configs import BASE_SEED, BF16, F16, F32, FP8_E4M3, GELU, SIGMOID, SOFTMAX, \
+    SWIGLU, LayerConfig
+from gen.inputs import make_inputs
+from oracle import moe_oracle as O
+from tests.harness import TOL_F32, check_routing, full_parity, gpu_layer, np_stored, \
+    rel_l2, say, spec, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def small(name, T, H, E, k, I, act_dtype=BF16, w_dtype=None, gate=SOFTMAX, renorm=False,
+          act=SWIGLU, e_begin=0, e_end=None, bias=None, remote=False, seed_off=0):
+    return LayerConfig(name, T=T, H=H, E=E, k=k, I=I, act_dtype=act_dtype,
+                       w_dtype=w_dtype or act_dtype, gate=gate, renorm=renorm, act=act,
+                       e_begin=e_begin, e_end=E if e_end is None else e_end,
+                       seed=BASE_SEED + 100 + seed_off, bias=bias, remote_rows=remote)
+
+
+GRID = [
+    small("bf16_tiles", 1000, 512, 8, 2, 256, renorm=True, bias="normal", seed_off=1),
+    small("f16_e16", 777, 256, 16, 4, 128, act_dtype=F16, seed_off=2),
+    small("bf16_ep_share", 300, 256, 64, 6, 128, gate=SIGMOID, e_begin=8, e_end=40,
+          remote=True, seed_off=3),
+    small("f32_gelu", 255, 128, 8, 2, 256, act_dtype=F32, act=GELU, seed_off=4),
+    small("fp8_ep_share", 64, 256, 256, 8, 128, w_dtype=FP8_E4M3, gate=SIGMOID,
+          e_begin=0, e_end=32, remote=True, seed_off=5),
+    small("bf16_router_mfma", 129, 256, 256, 8, 128, gate=SIGMOID, seed_off=6),
+    small("dense_e1", 100, 256, 1, 1, 128, renorm=True, seed_off=7),
+    small("k_equals_e", 50, 256, 4, 4, 128, seed_off=8),
+    small("one_token", 1, 256, 8, 2, 128, seed_off=9),
+    small("bf16_gelu", 200, 256, 8, 2, 256, act=GELU, seed_off=10),
+    small("no_local_expert", 90, 256, 8, 2, 128, e_begin=4, e_end=4, remote=True,
+          seed_off=11),
+    small("f16_e64_k1", 513, 256, 64, 1, 128, act_dtype=F16, seed_off=12),
+]
+
+
+@pytest.mark.parametrize("cfg", GRID, ids=[c.name for c in GRID])
+def test_small_layer_parity(cfg):
+    inp = make_inputs(cfg, "cpu")
+    lay = gpu_layer(cfg, to_device(inp))
+    res = full_parity(cfg, inp, lay)
+    say(f"  {cfg.name}: out rel-L2 {res['out_rel']:.3e}, flips {res['flips']}")
+
+
+def test_all_tokens_on_one_expert():
+    cfg = small("hot_expert", 600, 256, 8, 1, 128, seed_off=20)
+    inp = make_inputs(cfg, "cpu")
+    bias = torch.zeros(8, dtype=torch.float32)
+    bias[3] = 100.0
+    inp["bias"] = bias
+    lay = gpu_layer(cfg.with_(bias="normal"), to_device(inp))
+    counts = lay.counts.cpu().numpy()
+    assert counts.tolist() == [0, 0, 0, 600, 0, 0, 0, 0]
+    full_parity(cfg.with_(bias="normal"), inp, lay)
+
+
+def test_empty_input():
+    cfg = small("empty", 0, 256, 8, 2, 128, seed_off=21)
+    inp = make_inputs(cfg, "cpu")
+    lay = gpu_layer(cfg, to_device(inp))
+    assert lay.counts.cpu().tolist() == [0] * 8
+    assert lay.offsets.cpu().tolist() == [0] * 9
+
+
+def test_mass_ties_in_scores():
+    """Scores in {-1, -0, +0, 1}: selection must follow (score desc, index asc)."""
+    from combine_moe_route_02_amd import MoELayer
+    for E, k in [(16, 4), (256, 8), (8, 8), (1024, 32)]:
+        cfg = small(f"ties_{E}", 500, 256, E, k, 128, seed_off=30 + E)
+        lay = MoELayer(spec(cfg), "cuda")
+        g = torch.Generator().manual_seed(E)
+        s = torch.randint(-1, 2, (500, E), generator=g).float()
+        s[torch.rand((500, E), generator=g) < 0.2] = -0.0
+        say(f"[gpu] route ties E={E} k={k}")
+        lay.logits.copy_(s.cuda())
+        lay.route_from_logits()
+        torch.cuda.synchronize()
+        idx, w = O.route(s.numpy(), None, k, "softmax", False)
+        assert np.array_equal(lay.topk_idx.cpu().numpy(), idx)
+        assert rel_l2(lay.topk_w.cpu().numpy(), w) <= TOL_F32
+
+
+def test_gate_variants_on_given_scores():
+    """Temperature, sigmoid and renormalisation on the same scores."""
+    from combine_moe_route_02_amd import MoELayer
+    g = torch.Generator().manual_seed(5)
+    s = torch.randn((300, 64), generator=g) * 2
+    bias = torch.randn(64, generator=g)
+    for gate, renorm, invt in [("softmax", False, 1 / 0.3), ("softmax", True, 1.0),
+                               ("sigmoid", True, 1.0), ("softmax", False, 0.0)]:
+        cfg = small("gates", 300, 256, 64, 6, 128, gate=gate, renorm=renorm)
+        cfg = cfg.with_(inv_temperature=invt)
+        lay = MoELayer(spec(cfg), "cuda")
+        lay.logits.copy_(s.cuda())
+        say(f"[gpu] route gate={gate} renorm={renorm} inv_t={invt}")
+        lay.route_from_logits(bias.cuda())
+        torch.cuda.synchronize()
+        idx, w = O.route(s.numpy(), bias.numpy(), 6, gate, renorm, invt)
+        assert np.array_equal(lay.topk_idx.cpu().numpy(), idx)
+        assert rel_l2(lay.topk_w.cpu().numpy(), w) <= TOL_F32
+
+
+def test_repeat_runs_are_bitwise_identical():
+    cfg = GRID[0]
+    inp = to_device(make_inputs(cfg, "cpu"))
+    a = gpu_layer(cfg, inp)
+    b = gpu_layer(cfg, inp)
+    for name in ["logits", "topk_idx", "topk_w", "counts", "offsets", "slot_of",
+                 "row_token", "y_perm", "out"]:
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    r1 = int(a.offsets[cfg.e_end])           # rows written by dispatch and the FFN
+    assert torch.equal(a.x_perm[:r1], b.x_perm[:r1])
+    assert torch.equal(a.h[:r1], b.h[:r1])
