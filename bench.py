@@ -1,0 +1,261 @@
+"""Benchmark of the MoE-layer forward on one MI355X.
+
+One step = route -> dispatch -> expert FFN (GEMM-1 + SwiGLU, GEMM-2) ->
+combine over one batch of synthetic tokens, every step through the C ABI of
+libmoe.so on one HIP stream, inputs already resident in HBM.
+
+    python bench.py [--steps K] [--warmup W] [--config c2] [--gpus 1]
+
+Prints one JSON line: whole-layer tokens/s, plus the dominant kernel's
+roofline (GEMM-1, timed live with HIP events on the launch stream), the
+dispatch+combine HBM rate and grouped-GEMM MFMA utilisation, and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0           # MI355X HBM3E
+PEAK_MFMA_TFLOPS = 2500.0        # dense bf16 / fp16 MFMA
+METRIC = "MoE-layer tokens/sec on 1 GPU; dispatch+combine HBM GB/s; GEMM MFMA % of peak"
+WORKLOAD = {
+    "c1": "tiny fp32 layer: T=256, H=128, E=8, top-2 softmax, GELU FFN 128->256->128",
+    "c2": "ThunderEP section 1.2 shape, fp16: T=4096, H=4096, E=8, top-1 softmax, "
+          "SwiGLU FFN 4096->14336->4096",
+    "c3": "Mixtral-8x7B-like, bf16: T=8192, H=4096, E=8, top-2 renormalised softmax "
+          "with per-expert bias, SwiGLU 4096->14336->4096",
+    "c4": "DeepSeek-V3-like EP share, bf16: T=16384, H=7168, 256 experts (32 local), "
+          "top-8 sigmoid, Zipf load, SwiGLU 7168->2048->7168",
+    "c5": "decode batch, bf16 activations, fp8 e4m3 experts: T=128, H=7168, 256 experts "
+          "(32 local), top-8 sigmoid, SwiGLU 7168->2048->7168",
+}
+DT_NAME = {"f32": "f32", "f16": "f16", "bf16": "bf16"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0)
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "combine_moe_route_02_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_key}_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("#") or "=" not in line:
+                continue
+            k, v = line.split("=", 1)
+            rec[k.strip()] = v.strip()
+    if rec.get("source_hash") != source_hash():
+        return None
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this "
+              "build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from gen.configs import CONFIGS
+    from gen.inputs import make_inputs
+    from combine_moe_route_02_amd import LayerSpec, MoELayer
+    from combine_moe_route_02_amd._lib import lib
+
+    lib()  # fail loudly if the HIP library is missing
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {cfg.name} inputs on {dev}", file=sys.stderr, flush=True)
+    inp = make_inputs(cfg, dev)
+    tdt = inp["x"].dtype
+    spec = LayerSpec(T=cfg.T, H=cfg.H, E=cfg.E, k=cfg.k, I=cfg.I, act_dtype=tdt,
+                     gate=cfg.gate, renorm=cfg.renorm, act=cfg.act, e_begin=cfg.e_begin,
+                     e_end=cfg.e_end, inv_temperature=cfg.inv_temperature)
+    lay = MoELayer(spec, dev)
+    if inp["y_remote"] is not None:
+        lay.y_perm.copy_(inp["y_remote"])
+    x, wr, bias = inp["x"], inp["w_router"], inp["bias"]
+    w13, w2, s13, s2 = inp["w13"], inp["w2"], inp["w13_scale"], inp["w2_scale"]
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        lay.route(x, wr, bias)
+        lay.dispatch(x)
+        if ev is not None:
+            ev[0].record(stream)
+        lay.ffn_up(w13, s13)
+        if ev is not None:
+            ev[1].record(stream)
+        lay.ffn_down(w2, s2)
+        lay.combine()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # -- timed region: exactly K steps ------------------------------------
+    K = args.steps
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(K):
+        step(kev[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / K
+    gemm1_ms = float(np.mean([a.elapsed_time(b) for a, b in kev]))
+    print(f"[bench] {K} steps: {ms_per_step:.4f} ms/step (wall {wall:.3f} s)",
+          file=sys.stderr, flush=True)
+
+    # -- per-stage times (outside the timed region) ------------------------
+    names = ["route", "dispatch", "ffn_up", "ffn_down", "combine"]
+    calls = [lambda: lay.route(x, wr, bias), lambda: lay.dispatch(x),
+             lambda: lay.ffn_up(w13, s13), lambda: lay.ffn_down(w2, s2),
+             lambda: lay.combine()]
+    reps = max(3, min(K, 10))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+          for _ in range(reps)]
+    for r in range(reps):
+        ev[r][0].record(stream)
+        for j, c in enumerate(calls):
+            c()
+            ev[r][j + 1].record(stream)
+    torch.cuda.synchronize()
+    stage_ms = {n: float(np.median([ev[r][j].elapsed_time(ev[r][j + 1])
+                                    for r in range(reps)])) for j, n in enumerate(names)}
+
+    # -- algorithmic bytes and flops from this run's counts ---------------
+    counts = lay.counts.cpu().numpy().astype(np.int64)
+    idx = lay.topk_idx.cpu().numpy()
+    e0, e1 = cfg.e_begin, cfg.e_end
+    rows_loc = int(counts[e0:e1].sum())
+    ab = x.element_size()
+    H, I, T, k, E = cfg.H, cfg.I, cfg.T, cfg.k, cfg.E
+    loc_pick = (idx >= e0) & (idx < e1)
+    tok_needed = int(loc_pick.any(axis=1).sum())
+    disp_bytes = (tok_needed * H * ab + rows_loc * H * ab          # gather
+                  + T * k * 4 * 3 + E * 4 * 2)                    # idx in, slot/row out
+    comb_bytes = T * k * H * ab + T * H * ab + T * k * 8          # rows in, out, slot+w
+    dc_gbps = (disp_bytes + comb_bytes) / ((stage_ms["dispatch"] + stage_ms["combine"]) * 1e6)
+    touched = int((counts[e0:e1] > 0).sum())
+    if cfg.w_dtype == "e4m3":
+        wb1 = touched * 2 * I * H * 1 + touched * (2 * I // 128) * (H // 128) * 4
+    else:
+        wb1 = touched * 2 * I * H * w13.element_size()
+    flops1 = 2.0 * rows_loc * H * 2 * I
+    flops2 = 2.0 * rows_loc * I * H
+    gemm_tflops = (flops1 + flops2) / ((stage_ms["ffn_up"] + stage_ms["ffn_down"]) * 1e9)
+    if cfg.w_dtype == "e4m3":
+        bytes1 = wb1 + rows_loc * H * ab + rows_loc * I * ab
+        achieved = bytes1 / (gemm1_ms * 1e6)
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4)}
+    else:
+        achieved = flops1 / (gemm1_ms * 1e9)
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_MFMA_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4)}
+    roof["kernel"] = "grouped_gemm_mfma (GEMM-1 + SwiGLU, moe_expert_ffn_up)"
+    roof["avg_launch_ms"] = round(gemm1_ms, 5)
+    roof["traffic"] = load_traffic("gemm1", cfg.name)
+
+    res = {
+        "metric": METRIC,
+        "value": round(T / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DT_NAME[cfg.act_dtype] + ("+e4m3w" if cfg.w_dtype == "e4m3" else ""),
+        "data": "synthetic (seeded generator; random-init weights)",
+        "config": {"workload": f"{cfg.name}: {WORKLOAD[cfg.name]}", "tokens": T,
+                   "hidden": H, "experts": E, "local_experts": e1 - e0, "top_k": k,
+                   "ffn_inner": I, "local_rows": rows_loc},
+        "roofline": roof,
+        "stages_ms": {n: round(v, 5) for n, v in stage_ms.items()},
+        "dispatch_combine_GBps": round(dc_gbps, 1),
+        "dispatch_combine_frac_hbm": round(dc_gbps / PEAK_HBM_GBPS, 4),
+        "gemm_TFLOPs": round(gemm_tflops, 1),
+        "gemm_frac_mfma": round(gemm_tflops / PEAK_MFMA_TFLOPS, 4),
+        "source_hash": source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(cfg, inp, sample_tokens: int):
+    """The oracle, as it stands, on the first S tokens of the same workload."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    from oracle.torch_io import stored
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    S = sample_tokens or {"c1": 256, "c2": 256, "c3": 256, "c4": 128, "c5": 128}[cfg.name]
+    S = min(S, cfg.T)
+    print(f"[bench] cpu oracle on {S} tokens", file=sys.stderr, flush=True)
+    st = {k: (stored(v) if v is not None else None) for k, v in inp.items()}
+    sub = cfg.with_(T=S)
+    p = O.LayerParams(T=S, H=sub.H, E=sub.E, k=sub.k, I=sub.I, act_dtype=sub.act_dtype,
+                      w_dtype=sub.w_dtype, gate=sub.gate, renorm=sub.renorm, act=sub.act,
+                      e_begin=sub.e_begin, e_end=sub.e_end,
+                      inv_temperature=sub.inv_temperature)
+    yr = st["y_remote"][: S * cfg.k] if st["y_remote"] is not None else None
+    t0 = time.perf_counter()
+    O.layer_forward(p, st["x"][:S], st["w_router"], st["bias"], st["w13"], st["w2"],
+                    st["w13_scale"], st["w2_scale"], yr)
+    dt = time.perf_counter() - t0
+    return {"value": round(S / dt, 2), "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"first {S} of {cfg.T} tokens of the {cfg.name} layer, full "
+                      f"expert weights, float64 numpy oracle; {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

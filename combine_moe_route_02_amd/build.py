@@ -22,6 +22,7 @@ SOURCES = ["api.hip", "route.hip", "dispatch.hip", "gemm.hip", "combine.hip",
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-disable-promote-alloca-to-lds",
          "-I", os.path.join(ROOT, "include")]
 
 

@@ -26,6 +26,8 @@
 // fp8 E4M3 weights are decoded and scaled by their 128x128 tile scale while
 // being staged to LDS as bf16.
 
+#include <math.h>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -50,59 +52,88 @@ struct TileInfo {
   int g, r0, r1, base;
 };
 
-// Finds the group and row range of global m-tile `mt` from the device-side
-// offsets.  Every thread of the block must call it; returns false (for the
-// whole block) when the slot is beyond the last tile.
+// Per-workgroup table of m-tiles: s_pre[g] = number of m-tiles of groups
+// 0..g (inclusive prefix), built once from the device-side offsets.  Returns
+// the total number of m-tiles.  All threads must call it.
 template <int NT, int BM>
-__device__ bool locate_mtile(const GemmArgs& p, int mt, int* s_scan, int* s_res,
-                             TileInfo& ti) {
+__device__ int build_mtile_table(const GemmArgs& p, int* s_pre, int* s_tmp) {
   if (p.offsets == nullptr) {
-    const int tiles = (p.dense_M + BM - 1) / BM;
-    if (mt >= tiles) return false;
+    if (threadIdx.x == 0) s_pre[0] = (p.dense_M + BM - 1) / BM;
+    __syncthreads();
+    return s_pre[0];
+  }
+  int carry = 0;
+  for (int b = 0; b < p.n_groups; b += NT) {
+    const int g = b + (int)threadIdx.x;
+    int tiles = 0;
+    if (g < p.n_groups) {
+      const int o0 = p.offsets[p.e_begin + g];
+      const int o1 = p.offsets[p.e_begin + g + 1];
+      tiles = (o1 - o0 + BM - 1) / BM;
+    }
+    const int incl = block_incl_scan<NT>(tiles, s_tmp) + carry;
+    if (g < p.n_groups) s_pre[g] = incl;
+    carry += s_tmp[NT - 1];
+    __syncthreads();
+  }
+  return carry;
+}
+
+// m-tile index -> group and row range (binary search in the prefix table).
+template <int BM>
+__device__ __forceinline__ TileInfo tile_rows(const GemmArgs& p, const int* s_pre, int mt) {
+  TileInfo ti;
+  if (p.offsets == nullptr) {
     ti.g = 0;
     ti.r0 = mt * BM;
     ti.r1 = p.dense_M;
     ti.base = 0;
-    return true;
+    return ti;
   }
-  if (threadIdx.x == 0) s_res[0] = -1;
-  int carry = 0;
-  for (int b = 0; b < p.n_groups; b += NT) {
-    const int g = b + (int)threadIdx.x;
-    int o0 = 0, o1 = 0, tiles = 0;
-    if (g < p.n_groups) {
-      o0 = p.offsets[p.e_begin + g];
-      o1 = p.offsets[p.e_begin + g + 1];
-      tiles = (o1 - o0 + BM - 1) / BM;
-    }
-    const int incl = block_incl_scan<NT>(tiles, s_scan) + carry;
-    const int excl = incl - tiles;
-    if (tiles > 0 && mt >= excl && mt < incl) {
-      s_res[0] = g;
-      s_res[1] = o0 + (mt - excl) * BM;
-      s_res[2] = o1;
-    }
-    carry += s_scan[NT - 1];
-    __syncthreads();
-    if (s_res[0] >= 0) break;
+  int lo = 0, hi = p.n_groups - 1;   // first g with s_pre[g] > mt
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (s_pre[mid] > mt) hi = mid; else lo = mid + 1;
   }
-  if (s_res[0] < 0) return false;
-  ti.g = s_res[0];
-  ti.r0 = s_res[1];
-  ti.r1 = s_res[2];
+  const int before = lo > 0 ? s_pre[lo - 1] : 0;
+  ti.g = lo;
   ti.base = p.offsets[p.e_begin];
-  return true;
+  ti.r0 = p.offsets[p.e_begin + lo] + (mt - before) * BM;
+  ti.r1 = p.offsets[p.e_begin + lo + 1];
+  return ti;
 }
 
-// logical tile id -> (m-tile slot, n-tile), XCD-aware and banded.
-__device__ __forceinline__ void tile_coords(const GemmArgs& p, int& mt, int& nt) {
-  const int G8 = (int)gridDim.x >> 3;
-  const int bid = (int)blockIdx.x;
-  const int logical = (bid & 7) * G8 + (bid >> 3);
-  const int band = p.gm * p.n_tiles;
-  const int within = logical % band;
-  nt = within / p.gm;
-  mt = (logical / band) * p.gm + within % p.gm;
+// Tile t of the band order -> (m-tile, n-tile).  Bands hold gm m-tiles (the
+// last band may hold fewer); inside a band the m-tile index runs fastest.
+__device__ __forceinline__ void band_coords(int t, int total_m, int n_tiles, int gm,
+                                            int& mt, int& nt) {
+  const int full = total_m / gm;
+  const int per_band = gm * n_tiles;
+  const int band = t / per_band;
+  if (band < full) {
+    const int w = t - band * per_band;
+    nt = w / gm;
+    mt = band * gm + w % gm;
+  } else {
+    const int gl = total_m - full * gm;
+    const int w = t - full * per_band;
+    nt = w / gl;
+    mt = full * gm + w % gl;
+  }
+}
+
+// The share of tiles [lo, hi) of this workgroup's XCD and its stride.  The
+// hardware places workgroup i on XCD i % 8, so the persistent grid (a
+// multiple of 8) gives every XCD gridDim/8 workgroups and a contiguous,
+// equal slice of the tile order.
+__device__ __forceinline__ void xcd_share(int total, int& first, int& end, int& stride) {
+  const int xcd = (int)blockIdx.x & 7;
+  const int per = (int)gridDim.x >> 3;
+  const long long lo = (long long)total * xcd / 8;
+  const long long hi = (long long)total * (xcd + 1) / 8;
+  first = (int)lo + ((int)blockIdx.x >> 3);
+  end = (int)hi;
+  stride = per;
 }
 
 template <int DT>
@@ -131,9 +162,9 @@ __device__ __forceinline__ float gelu_erf(float a) {
 }
 
 // 16 fp8 codes * scale -> 16 bf16 (two 16-byte chunks).
-__device__ __forceinline__ void fp8x16_to_bf16(const uint4& q, float s, uint4& lo,
-                                               uint4& hi) {
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+__device__ __forceinline__ void fp8x16_to_bf16(const u32x4& q, float s, u32x4& lo,
+                                               u32x4& hi) {
+  const uint32_t w[4] = {q[0], q[1], q[2], q[3]};
   uint32_t o[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -145,8 +176,8 @@ __device__ __forceinline__ void fp8x16_to_bf16(const uint4& q, float s, uint4& l
     o[2 * i] = (uint32_t)b0 | ((uint32_t)b1 << 16);
     o[2 * i + 1] = (uint32_t)b2 | ((uint32_t)b3 << 16);
   }
-  lo = make_uint4(o[0], o[1], o[2], o[3]);
-  hi = make_uint4(o[4], o[5], o[6], o[7]);
+  lo = u32x4{o[0], o[1], o[2], o[3]};
+  hi = u32x4{o[4], o[5], o[6], o[7]};
 }
 
 template <int DT, int WK, int EPI, int BM, int BN, int WM, int WN>
@@ -164,27 +195,32 @@ __global__ void __launch_bounds__(WM * WN * 64)
 
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];
+  __shared__ int s_pre[1024];
   __shared__ int s_scan[NT];
-  __shared__ int s_res[3];
 
+  const int total_m = build_mtile_table<NT, BM>(p, s_pre, s_scan);
+  int t_first, t_end, t_stride;
+  xcd_share(total_m * p.n_tiles, t_first, t_end, t_stride);
+  for (int t = t_first; t < t_end; t += t_stride) {
   int mt, nt;
-  tile_coords(p, mt, nt);
-  if (mt >= p.mt_slots) return;
-  TileInfo ti;
-  if (!locate_mtile<NT, BM>(p, mt, s_scan, s_res, ti)) return;
+  band_coords(t, total_m, p.n_tiles, p.gm, mt, nt);
+  const TileInfo ti = tile_rows<BM>(p, s_pre, mt);
 
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const long long a_sub = p.a_local ? ti.base : 0;
-  const long long c_sub = p.c_local ? ti.base : 0;
+  const int a_sub = p.a_local ? ti.base : 0;
+  const int c_sub = p.c_local ? ti.base : 0;
   const int n0 = nt * BN;
   const int n0h = nt * (BN / 2);
 
-  // Source addresses and LDS slots of this thread's chunks.
-  const uint16_t* Ag = (const uint16_t*)p.A;
-  const uint16_t* a_src[ACH];
+  // Chunk addresses: 64-bit for activation rows, 32-bit byte offsets from the
+  // expert's (uniform) base for weights; the host keeps one expert's weight
+  // matrix below 4 GiB.
+  const char* Abase = (const char*)p.A;
+  const char* Bbase = (const char*)p.B + (long long)ti.g * p.strideB * (WK == W_FP8 ? 1 : 2);
+  const char* a_ptr[ACH];
   int a_lds[ACH];
 #pragma unroll
   for (int i = 0; i < ACH; ++i) {
@@ -192,14 +228,14 @@ __global__ void __launch_bounds__(WM * WN * 64)
     const int row = c >> 3, kc = c & 7;
     int grow = ti.r0 + row;
     grow = grow < ti.r1 ? grow : ti.r1 - 1;
-    long long arow = grow - a_sub;
+    int arow = grow - a_sub;
     if (p.a_local && arow >= p.a_rows) arow = p.a_rows - 1;
-    a_src[i] = Ag + arow * p.lda + kc * 8;
+    a_ptr[i] = Abase + ((long long)arow * p.lda + kc * 8) * 2;
     a_lds[i] = row * BK + ((kc ^ (row & 7)) << 3);
   }
-  const uint8_t* b_src[BCH];
-  int b_lds[BCH];
-  const float* s_src[BCH];
+  uint32_t b_off[BCH];
+  int b_lds[BCH], b_lds2[BCH];
+  uint32_t s_off[BCH];
 #pragma unroll
   for (int i = 0; i < BCH; ++i) {
     const int c = tid + i * NT;
@@ -212,52 +248,18 @@ __global__ void __launch_bounds__(WM * WN * 64)
     } else {
       n = n0 + row;
     }
-    const long long eoff = (long long)ti.g * p.strideB + (long long)n * p.ldb;
     if (WK == W_FP8) {
-      b_src[i] = (const uint8_t*)p.B + eoff + kc * 8;
-      s_src[i] = p.Bscale + (long long)ti.g * p.strideS +
-                 (long long)(n >> 7) * (p.K >> 7);
+      b_off[i] = (uint32_t)n * (uint32_t)p.ldb + kc * 8;
+      s_off[i] = (uint32_t)(n >> 7) * (uint32_t)(p.K >> 7);
+      b_lds2[i] = row * BK + (((kc + 1) ^ (row & 7)) << 3);
     } else {
-      b_src[i] = (const uint8_t*)p.B + (eoff + kc * 8) * 2;
-      s_src[i] = nullptr;
+      b_off[i] = ((uint32_t)n * (uint32_t)p.ldb + kc * 8) * 2u;
+      s_off[i] = 0;
+      b_lds2[i] = 0;
     }
     b_lds[i] = row * BK + ((kc ^ (row & 7)) << 3);
   }
-
-  uint4 ra[ACH], rb[BCH];
-  float rs[BCH];
-  auto load_tiles = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) ra[i] = *(const uint4*)(a_src[i] + k0);
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-      if (WK == W_FP8) {
-        rb[i] = *(const uint4*)(b_src[i] + k0);
-        rs[i] = s_src[i][k0 >> 7];
-      } else {
-        rb[i] = *(const uint4*)(b_src[i] + (long long)k0 * 2);
-      }
-    }
-  };
-  auto store_tiles = [&](int buf) {
-    uint16_t* As = sA[buf];
-    uint16_t* Bs = sB[buf];
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) *(uint4*)(As + a_lds[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-      if (WK == W_FP8) {
-        uint4 lo, hi;
-        fp8x16_to_bf16(rb[i], rs[i], lo, hi);
-        const int row = b_lds[i] / BK;
-        const int kc = ((b_lds[i] % BK) >> 3) ^ (row & 7);
-        *(uint4*)(Bs + b_lds[i]) = lo;
-        *(uint4*)(Bs + row * BK + (((kc + 1) ^ (row & 7)) << 3)) = hi;
-      } else {
-        *(uint4*)(Bs + b_lds[i]) = rb[i];
-      }
-    }
-  };
+  const float* Sbase = (WK == W_FP8) ? p.Bscale + (long long)ti.g * p.strideS : nullptr;
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -268,15 +270,52 @@ __global__ void __launch_bounds__(WM * WN * 64)
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int nk = p.K / BK;
-  load_tiles(0);
-  store_tiles(0);
+
+  // Prologue: k-step 0 straight to buffer 0.
+  {
+  u32x4 ra[ACH], rb[BCH];
+  float rs[BCH];
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) ra[i] = *(const u32x4*)(a_ptr[i]);
+#pragma unroll
+  for (int i = 0; i < BCH; ++i) {
+    rb[i] = *(const u32x4*)(Bbase + b_off[i]);
+    if (WK == W_FP8) rs[i] = Sbase[s_off[i]];
+  }
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) *(u32x4*)(&sA[0][a_lds[i]]) = ra[i];
+#pragma unroll
+  for (int i = 0; i < BCH; ++i) {
+    if (WK == W_FP8) {
+      u32x4 lo, hi;
+      fp8x16_to_bf16(rb[i], rs[i], lo, hi);
+      *(u32x4*)(&sB[0][b_lds[i]]) = lo;
+      *(u32x4*)(&sB[0][b_lds2[i]]) = hi;
+    } else {
+      *(u32x4*)(&sB[0][b_lds[i]]) = rb[i];
+    }
+  }
+  }
   __syncthreads();
 
   const int lrow = lane & 31;
   const int khalf = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) load_tiles((kt + 1) * BK);
+    const bool more = kt + 1 < nk;
+    u32x4 ra[ACH], rb[BCH];
+    float rs[BCH];
+    if (more) {
+      const uint32_t ka = (uint32_t)(kt + 1) * BK * 2u;
+      const uint32_t kb = (uint32_t)(kt + 1) * BK * (WK == W_FP8 ? 1u : 2u);
+#pragma unroll
+      for (int i = 0; i < ACH; ++i) ra[i] = *(const u32x4*)(a_ptr[i] + ka);
+#pragma unroll
+      for (int i = 0; i < BCH; ++i) {
+        rb[i] = *(const u32x4*)(Bbase + b_off[i] + kb);
+        if (WK == W_FP8) rs[i] = Sbase[s_off[i] + (((kt + 1) * BK) >> 7)];
+      }
+    }
     const uint16_t* As = sA[cur];
     const uint16_t* Bs = sB[cur];
 #pragma unroll
@@ -295,7 +334,23 @@ __global__ void __launch_bounds__(WM * WN * 64)
         for (int j = 0; j < TN; ++j)
           acc[i][j] = MfmaOp<DT>::run(af[i], bfv[j], acc[i][j]);
     }
-    if (kt + 1 < nk) store_tiles(cur ^ 1);
+    if (more) {
+      uint16_t* An = sA[cur ^ 1];
+      uint16_t* Bn = sB[cur ^ 1];
+#pragma unroll
+      for (int i = 0; i < ACH; ++i) *(u32x4*)(An + a_lds[i]) = ra[i];
+#pragma unroll
+      for (int i = 0; i < BCH; ++i) {
+        if (WK == W_FP8) {
+          u32x4 lo, hi;
+          fp8x16_to_bf16(rb[i], rs[i], lo, hi);
+          *(u32x4*)(Bn + b_lds[i]) = lo;
+          *(u32x4*)(Bn + b_lds2[i]) = hi;
+        } else {
+          *(u32x4*)(Bn + b_lds[i]) = rb[i];
+        }
+      }
+    }
     __syncthreads();
   }
 
@@ -334,6 +389,7 @@ __global__ void __launch_bounds__(WM * WN * 64)
       }
     }
   }
+  }  // tile loop
 }
 
 // Plain fp32 grouped GEMM (64x64 tiles, 4x4 outputs per thread).
@@ -342,14 +398,16 @@ __global__ void __launch_bounds__(256) grouped_gemm_f32(GemmArgs p) {
   constexpr int BM = 64, BN = 64, BK = 16, NT = 256;
   __shared__ float sA[BM][BK + 1];
   __shared__ float sB[BN][BK + 1];
+  __shared__ int s_pre[1024];
   __shared__ int s_scan[NT];
-  __shared__ int s_res[3];
 
+  const int total_m = build_mtile_table<NT, BM>(p, s_pre, s_scan);
+  int t_first, t_end, t_stride;
+  xcd_share(total_m * p.n_tiles, t_first, t_end, t_stride);
+  for (int t = t_first; t < t_end; t += t_stride) {
   int mt, nt;
-  tile_coords(p, mt, nt);
-  if (mt >= p.mt_slots) return;
-  TileInfo ti;
-  if (!locate_mtile<NT, BM>(p, mt, s_scan, s_res, ti)) return;
+  band_coords(t, total_m, p.n_tiles, p.gm, mt, nt);
+  const TileInfo ti = tile_rows<BM>(p, s_pre, mt);
 
   const int tid = (int)threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
@@ -412,6 +470,8 @@ __global__ void __launch_bounds__(256) grouped_gemm_f32(GemmArgs p) {
       }
     }
   }
+  __syncthreads();
+  }  // tile loop
 }
 
 // ---------------------------------------------------------------------------
@@ -420,53 +480,101 @@ __global__ void __launch_bounds__(256) grouped_gemm_f32(GemmArgs p) {
 
 namespace {
 
-template <int BM>
-void size_grid(GemmArgs& a, int max_rows, int BN, int gm, dim3& grid) {
-  int slots;
-  if (a.offsets == nullptr)
-    slots = (a.dense_M + BM - 1) / BM;
-  else
-    slots = (max_rows + BM - 1) / BM + a.n_groups;
-  if (gm > slots) gm = slots;
-  if (gm < 1) gm = 1;
-  slots = (slots + gm - 1) / gm * gm;
-  a.mt_slots = slots;
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Persistent grid: no more workgroups than can be resident at once (so the
+// XCD placement i % 8 holds for all of them) and no more than the tile count
+// can use; always a multiple of 8.
+template <typename Kern>
+dim3 persistent_grid(Kern kernel, int threads, GemmArgs& a, int max_rows, int BM, int BN,
+                     int gm) {
+  static int occ = 0;  // one cache per kernel instantiation
+  if (occ == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess ||
+        n <= 0)
+      n = 1;
+    occ = n;
+  }
+  long long mtiles = a.offsets ? (long long)(max_rows + BM - 1) / BM + a.n_groups
+                               : (long long)(a.dense_M + BM - 1) / BM;
   a.n_tiles = a.Nb / BN;
-  a.gm = gm;
-  long long total = (long long)slots * a.n_tiles;
-  total = (total + 7) / 8 * 8;
-  grid = dim3((unsigned)total);
+  a.gm = gm < 1 ? 1 : gm;
+  a.mt_slots = (int)mtiles;
+  long long g = mtiles * a.n_tiles;
+  const long long cap = (long long)device_cus() * occ;
+  if (g > cap) g = cap;
+  g = (g + 7) / 8 * 8;
+  return dim3((unsigned)g);
 }
 
 template <int DT, int WK, int EPI, int BM, int BN, int WM, int WN>
 int run_mfma(GemmArgs a, int max_rows, int gm, hipStream_t s) {
   if (a.Nb % BN || a.K % 64) return MOE_ERR_UNSUPPORTED;
   if (WK == W_FP8 && (a.K % 128 || a.Nb % 128)) return MOE_ERR_UNSUPPORTED;
-  dim3 grid;
-  size_grid<BM>(a, max_rows, BN, gm, grid);
-  if (grid.x == 0) return MOE_OK;
-  hipLaunchKernelGGL((grouped_gemm_mfma<DT, WK, EPI, BM, BN, WM, WN>), grid,
-                     dim3(WM * WN * 64), 0, s, a);
+  if ((long long)a.Nb * a.ldb * (WK == W_FP8 ? 1 : 2) >= (1ll << 32))
+    return MOE_ERR_UNSUPPORTED;
+  if (a.offsets && a.n_groups > 1024) return MOE_ERR_UNSUPPORTED;
+  auto kern = grouped_gemm_mfma<DT, WK, EPI, BM, BN, WM, WN>;
+  const dim3 grid = persistent_grid(kern, WM * WN * 64, a, max_rows, BM, BN, gm);
+  hipLaunchKernelGGL(kern, grid, dim3(WM * WN * 64), 0, s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+// Relative MFMA efficiency of each tile shape (larger wave tiles need fewer
+// LDS reads per MFMA) used to pick a shape; rounds of 256 workgroups model the
+// tail of the last wave of tiles.
+struct TileShape {
+  int BM, BN;
+  float eff;
+};
+
 template <int DT, int WK, int EPI>
 int pick_tile(GemmArgs a, int max_rows, hipStream_t s) {
+  if (EPI == EPI_F32) return run_mfma<DT, WK, EPI, 64, 128, 2, 2>(a, max_rows, 4, s);
   const int groups = a.offsets ? a.n_groups : 1;
   const int rows = a.offsets ? max_rows : a.dense_M;
-  const int avg = rows / (groups > 0 ? groups : 1);
-  if (EPI == EPI_F32) return run_mfma<DT, WK, EPI, 64, 128, 2, 2>(a, max_rows, 4, s);
-  if (avg <= 64) return run_mfma<DT, WK, EPI, 32, 256, 1, 4>(a, max_rows, 1, s);
+  const double avg = (double)rows / (groups > 0 ? groups : 1);
+  if (avg <= 48.0) return run_mfma<DT, WK, EPI, 32, 256, 1, 4>(a, max_rows, 1, s);
+  const TileShape shapes[2] = {{256, 256, 1.0f}, {128, 256, 0.8f}};
+  int best = 0;
+  double best_t = 1e300;
+  for (int c = 0; c < 2; ++c) {
+    const TileShape& t = shapes[c];
+    if (a.Nb % t.BN) continue;
+    // expected m-tiles: a segment's ragged tail costs half a tile on average
+    const double mtiles = groups * (avg / t.BM + (a.offsets ? 0.5 : 1.0));
+    const double tiles = mtiles * (a.Nb / t.BN);
+    const double rounds = ceil(tiles / 256.0);
+    const double tm = rounds * (double)t.BM * t.BN / t.eff;
+    if (tm < best_t) {
+      best_t = tm;
+      best = c;
+    }
+  }
+  if (best == 0) return run_mfma<DT, WK, EPI, 256, 256, 2, 2>(a, max_rows, 4, s);
   return run_mfma<DT, WK, EPI, 128, 256, 2, 2>(a, max_rows, 4, s);
 }
 
 template <int EPI>
 int run_f32(GemmArgs a, int max_rows, hipStream_t s) {
   if (a.Nb % 64 || a.K % 16) return MOE_ERR_UNSUPPORTED;
-  dim3 grid;
-  size_grid<64>(a, max_rows, 64, 4, grid);
-  if (grid.x == 0) return MOE_OK;
-  hipLaunchKernelGGL((grouped_gemm_f32<EPI>), grid, dim3(256), 0, s, a);
+  if (a.offsets && a.n_groups > 1024) return MOE_ERR_UNSUPPORTED;
+  auto kern = grouped_gemm_f32<EPI>;
+  const dim3 grid = persistent_grid(kern, 256, a, max_rows, 64, 64, 4);
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
