@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0)
+    ap.add_argument("--fused", action="store_true",
+                    help="time the fused dispatch->GEMM->combine kernel instead of "
+                         "the four separate calls")
     return ap.parse_args()
 
 
@@ -114,9 +117,17 @@ def main():
 
     def step(ev=None):
         lay.route(x, wr, bias)
-        lay.dispatch(x)
+        if args.fused:
+            lay.dispatch_layout(x)
+        else:
+            lay.dispatch(x)
         if ev is not None:
             ev[0].record(stream)
+        if args.fused:
+            lay.fused(x, w13, w2)
+            if ev is not None:
+                ev[1].record(stream)
+            return
         lay.ffn_up(w13, s13)
         if ev is not None:
             ev[1].record(stream)
@@ -185,6 +196,8 @@ def main():
     flops1 = 2.0 * rows_loc * H * 2 * I
     flops2 = 2.0 * rows_loc * I * H
     gemm_tflops = (flops1 + flops2) / ((stage_ms["ffn_up"] + stage_ms["ffn_down"]) * 1e9)
+    if args.fused:
+        flops1 += flops2   # the fused kernel runs both GEMMs (and combine)
     if cfg.w_dtype == "e4m3":
         bytes1 = wb1 + rows_loc * H * ab + rows_loc * I * ab
         achieved = bytes1 / (gemm1_ms * 1e6)
@@ -194,7 +207,9 @@ def main():
         achieved = flops1 / (gemm1_ms * 1e9)
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_MFMA_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4)}
-    roof["kernel"] = "grouped_gemm_mfma (GEMM-1 + SwiGLU, moe_expert_ffn_up)"
+    roof["kernel"] = ("fused_layer_kernel (GEMM-1 + SwiGLU + GEMM-2 + combine, moe_layer_fused)"
+                      if args.fused else
+                      "grouped_gemm_dma (GEMM-1 + SwiGLU, moe_expert_ffn_up)")
     roof["avg_launch_ms"] = round(gemm1_ms, 5)
     roof["traffic"] = load_traffic("gemm1", cfg.name)
 
@@ -211,7 +226,8 @@ def main():
         "vs_baseline": None,
         "dtype": DT_NAME[cfg.act_dtype] + ("+e4m3w" if cfg.w_dtype == "e4m3" else ""),
         "data": "synthetic (seeded generator; random-init weights)",
-        "config": {"workload": f"{cfg.name}: {WORKLOAD[cfg.name]}", "tokens": T,
+        "config": {"workload": f"{cfg.name}: {WORKLOAD[cfg.name]}"
+                   + (" [fused kernel]" if args.fused else ""), "tokens": T,
                    "hidden": H, "experts": E, "local_experts": e1 - e0, "top_k": k,
                    "ffn_inner": I, "local_rows": rows_loc},
         "roofline": roof,

@@ -195,9 +195,9 @@ int moe_layer_fused(const void* x, const int32_t* offsets, const int32_t* slot_o
   if (e_begin < 0 || e_end < e_begin || e_end > E) return MOE_ERR_ARG;
   if (H % 256 || I % 128) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
-  if (!x || !offsets || !slot_of || !row_token || !topk_w || !w13 || !w2 || !h_ws ||
-      !y_perm || !out)
+  if (!x || !offsets || !slot_of || !row_token || !topk_w || !y_perm || !out)
     return MOE_ERR_ARG;
+  if (e_end > e_begin && (!w13 || !w2 || !h_ws)) return MOE_ERR_ARG;
   if (!ws || ws_bytes < fused_ws_bytes(T, H, E, k, I)) return MOE_ERR_WORKSPACE;
   return fused_impl(x, offsets, slot_of, row_token, topk_w, act_dtype, T, H, E, k, I,
                     e_begin, e_end, act, w13, w2, h_ws, y_perm, out, ws, ws_bytes, stream);

@@ -127,8 +127,15 @@ class MoELayer:
                           s.E, s.I, e0, e1, ACTS[s.act], w13, w2, self.h, self.y_perm,
                           self.out, self.ws_fused, stream=stream)
 
+    def dispatch_layout(self, x, stream=None):
+        """Counts, offsets and the layout map only (no permuted copy of x):
+        the fused kernel reads token rows through the layout map."""
+        s = self.spec
+        L.moe_dispatch(x, self.topk_idx, s.E, 0, 0, self.counts, self.offsets,
+                       self.slot_of, self.row_token, self.x_perm, self.ws, stream=stream)
+
     def forward_fused(self, x, w_router, bias, w13, w2, stream=None) -> torch.Tensor:
         self.route(x, w_router, bias, stream)
-        self.dispatch(x, stream)   # counts/offsets/layout; its gather is unused here
+        self.dispatch_layout(x, stream)
         self.fused(x, w13, w2, stream)
         return self.out

@@ -31,11 +31,11 @@ def test_c1_full():
     say(f"  c1 out rel-L2 {res['out_rel']:.3e}")
 
 
-def sampled_parity(cfg, inp, lay, n_tokens=48, seed=7):
+def sampled_parity(cfg, inp, lay, n_tokens=48, seed=7, check_xperm=True):
     """Bit-exact integer path over all tokens; float outputs on samples."""
     st = {"x": stored(inp["x"]), "w_router": stored(inp["w_router"]),
           "bias": stored(inp["bias"]) if inp["bias"] is not None else None}
-    r = check_routing(cfg, lay, st)
+    r = check_routing(cfg, lay, st, check_xperm)
     rng = np.random.default_rng(seed)
     toks = np.sort(rng.choice(cfg.T, size=min(n_tokens, cfg.T), replace=False))
 
