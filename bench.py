@@ -47,6 +47,14 @@ def parse():
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before the "
+                         "steps (the reference for HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"),
+                    help="turn two rocprofv3 counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--calib-copy-mib run into the per-launch HBM traffic summary")
+    ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "OUT"),
+                    help="turn a rocprofv3 --kernel-trace --stats CSV into a text summary")
     ap.add_argument("--fused", action="store_true",
                     help="time the fused dispatch->GEMM->combine kernel instead of "
                          "the four separate calls")
@@ -86,6 +94,12 @@ def load_traffic(kernel_key: str, workload: str):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        return pmc_summary(*args.pmc_summary, calib_mib=args.calib_copy_mib or 1024,
+                           workload=args.config)
+    if args.stats_summary:
+        return stats_summary(*args.stats_summary, workload=args.config,
+                             extra="--fused" if args.fused else "")
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this "
               "build has no multi-GPU path", file=sys.stderr)
@@ -134,6 +148,15 @@ def main():
         lay.ffn_down(w2, s2)
         lay.combine()
 
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)      # reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        del a, b
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -241,6 +264,96 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
     print(json.dumps(res), flush=True)
+
+
+def _counter_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _per_kernel(rows, counter):
+    """{kernel name: [value per dispatch]} for one counter."""
+    out = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def pmc_summary(fetch_csv, write_csv, out_path, calib_mib, workload):
+    """HBM traffic per GEMM-1 launch from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for the plain
+    copy of calib_mib MiB (true bytes: calib_mib MiB read and written)."""
+    import numpy as np
+    fetch = _per_kernel(_counter_rows(fetch_csv), "FETCH_SIZE")
+    write = _per_kernel(_counter_rows(write_csv), "WRITE_SIZE")
+    # the calibration copy is the runtime's buffer copy of calib_mib MiB
+    # (b.copy_(a) on contiguous uint8 tensors); take its largest dispatch
+    true_kib = calib_mib * 1024.0
+    cf = max(fetch.get("__amd_rocclr_copyBuffer", [0.0]))
+    cw = max(write.get("__amd_rocclr_copyBuffer", [0.0]))
+    if cf <= 0 or cw <= 0:
+        raise SystemExit("calibration copy not found in the counter CSVs")
+    f_scale, w_scale = true_kib / cf, true_kib / cw
+    def is_gemm1(name):
+        if "fused_layer" in name:
+            return True
+        if "grouped_gemm" not in name or "<" not in name:
+            return False
+        targs = [a.strip() for a in name.split("<", 1)[1].split(">", 1)[0].split(",")]
+        epi = targs[1] if "grouped_gemm_dma" in name else targs[2]  # SwiGLU epilogue = 1
+        return epi == "1"
+    gemm = [k for k in fetch if is_gemm1(k)]
+    lines = [f"# HBM traffic per launch of the GEMM-1 (+SwiGLU) kernel, workload {workload}",
+             "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two rocprofv3 --pmc runs,",
+             f"# each scaled by the same counter's reading for a plain {calib_mib} MiB copy",
+             f"# copy kernel: FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB "
+             f"(true {true_kib:.0f} KiB each) -> scales {f_scale:.4f}, {w_scale:.4f}",
+             "# commands (from /tmp, TMPDIR=/tmp, R = repository root):",
+             f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d <dir_f> -o pmc -- python3 $R/bench.py "
+             f"--config {workload} --steps 3 --warmup 1 --no-cpu-baseline --calib-copy-mib {calib_mib}",
+             f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d <dir_w> -o pmc -- python3 $R/bench.py "
+             f"--config {workload} --steps 3 --warmup 1 --no-cpu-baseline --calib-copy-mib {calib_mib}",
+             f"#   python3 $R/bench.py --config {workload} --calib-copy-mib {calib_mib} "
+             "--pmc-summary <dir_f>/pmc_counter_collection.csv <dir_w>/pmc_counter_collection.csv <out>"]
+    rec = {}
+    for k in gemm:
+        fk = float(np.median(fetch[k]))
+        wk = float(np.median(write.get(k, [0.0])))
+        hbm = (fk * f_scale + wk * w_scale) * 1024.0
+        lines.append(f"# kernel {k[:110]}: dispatches {len(fetch[k])}, "
+                     f"FETCH_SIZE {fk:.0f} KiB, WRITE_SIZE {wk:.0f} KiB, HBM {hbm / 1e6:.1f} MB")
+        rec.setdefault("hbm_bytes_per_launch", hbm)
+        rec.setdefault("fetch_kib_per_launch", fk)
+        rec.setdefault("write_kib_per_launch", wk)
+    lines.append(f"source_hash = {source_hash()}")
+    for key, v in rec.items():
+        lines.append(f"{key} = {v:.0f}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def stats_summary(stats_csv, out_path, workload="c2", extra=""):
+    rows = _counter_rows(stats_csv)
+    keys = list(rows[0].keys()) if rows else []
+    name_k = "Name" if "Name" in keys else keys[0]
+    lines = ["# rocprofv3 --kernel-trace --stats: per-kernel totals (ns), workload " + workload,
+             "# command (from /tmp, TMPDIR=/tmp, R = repository root):",
+             "#   rocprofv3 --kernel-trace --stats -f csv -d <dir> -o st -- python3 $R/bench.py "
+             f"--config {workload} --steps 5 --warmup 2 --no-cpu-baseline {extra}".rstrip(),
+             f"#   python3 $R/bench.py --config {workload} --stats-summary "
+             "<dir>/st_kernel_stats.csv <out>",
+             "# input generation kernels (torch elementwise ops) run before the timed steps",
+             "# " + ", ".join(["calls", "total_ns", "average_ns", "pct", "kernel"])]
+    for r in rows:
+        lines.append(f"{r.get('Calls', '')}, {r.get('TotalDurationNs', '')}, "
+                     f"{r.get('AverageNs', '')}, {r.get('Percentage', '')}, {r[name_k][:140]}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines[:30]))
 
 
 def cpu_baseline(cfg, inp, sample_tokens: int):
