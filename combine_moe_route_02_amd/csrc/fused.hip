@@ -134,8 +134,7 @@ __global__ void __launch_bounds__(WM * WN * 64) fused_layer_kernel(FusedArgs f) 
     __syncthreads();
     if (it < len1) {
       int mt, nt;
-      band_coords(lo1 + it, total_m, nt1, f.g1.gm, mt, nt);
-      const TileInfo ti = tile_rows<BM>(f.g1, s_pre, mt);
+      const TileInfo ti = band_tile<BM>(f.g1, s_pre, lo1 + it, nt1, f.g1.gm, mt, nt);
       T1::run(f.g1, ti, nt, smem, f.row_token);
       block_signal(cnt1 + mt);
       continue;
@@ -143,9 +142,8 @@ __global__ void __launch_bounds__(WM * WN * 64) fused_layer_kernel(FusedArgs f) 
     it -= len1;
     if (it < len2) {
       int mt, nt;
-      band_coords(lo2 + it, total_m, nt2, f.g2.gm, mt, nt);
+      const TileInfo ti = band_tile<BM>(f.g2, s_pre, lo2 + it, nt2, f.g2.gm, mt, nt);
       if (!block_wait(cnt1 + mt, nt1, err, &s_flag)) return;
-      const TileInfo ti = tile_rows<BM>(f.g2, s_pre, mt);
       T2::run(f.g2, ti, nt, smem, nullptr);
       block_signal(cnt2 + mt);
       continue;
@@ -269,7 +267,7 @@ int launch_fused(FusedArgs f, int max_rows, hipStream_t s) {
     return MOE_ERR_HIP;
   f.g1.n_tiles = f.g1.Nb / BN;
   f.g2.n_tiles = f.g2.Nb / BN;
-  f.g1.gm = f.g2.gm = 4;
+  f.g1.gm = f.g2.gm = 8;
   // grid within co-resident capacity (forward progress), a multiple of 8
   int grid = (cus * occ) / kQueues * kQueues;
   if (grid < kQueues) return MOE_ERR_UNSUPPORTED;

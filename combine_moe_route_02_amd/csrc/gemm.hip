@@ -7,17 +7,20 @@
 // Segment sizes are read on the device from `offsets`, so the grid is sized
 // from host-known upper bounds only and surplus workgroups exit at once.
 //
-// Tile order.  The 1-D grid is remapped so that consecutive logical tiles
-// land on the same XCD (hardware dispatches workgroup i to XCD i % 8), and
-// logical tiles walk bands of `gm` m-tiles for one n-tile before moving to
-// the next n-tile: the gm m-tiles of a band share each weight tile in that
-// XCD's L2, and a band's activation rows are reused across its n-tiles.
+// Tile order.  Persistent workgroups; each XCD (hardware dispatches
+// workgroup i to XCD i % 8) takes a contiguous slice of the logical tile
+// order, which keeps one expert's tiles together: all m-tiles of an expert
+// (in bands of at most `gm`) for one n-tile, then the next n-tile.  The
+// m-tiles of a band share each weight tile in that XCD's L2, so expert
+// weights are read from HBM about once, and a band's activation rows are
+// reused across its n-tiles.
 //
-// Main loop.  BK = 64; global -> registers -> LDS with a two-buffer ring and
-// one barrier per k-step; 16-byte chunks are stored XOR-swizzled
-// (chunk ^ (row & 7)) so that the ds_read_b128 of an MFMA operand (32 rows,
-// same k-chunk) touches every bank group once.  Each wave owns a
-// (BM/WM) x (BN/WN) accumulator block of 32x32 MFMA tiles
+// 16-bit weights (DmaTile): global -> LDS directly, four stages of BK = 32.
+// fp8 weights (register-staged kernel below): BK = 64; global -> registers
+// -> LDS with a two-buffer ring and one barrier per k-step; 16-byte chunks
+// are stored XOR-swizzled (chunk ^ (row & 7)) so that the ds_read_b128 of an
+// MFMA operand (32 rows, same k-chunk) touches every bank group once.  Each
+// wave owns a (BM/WM) x (BN/WN) accumulator block of 32x32 MFMA tiles
 // (v_mfma_f32_32x32x16_{bf16,f16}: 8 values of K per lane per operand).
 //
 // Epilogues: plain store in the activation dtype, SwiGLU (the B tile
@@ -76,8 +79,7 @@ __global__ void __launch_bounds__(WM * WN * 64)
   xcd_share(total_m * p.n_tiles, t_first, t_end, t_stride);
   for (int t = t_first; t < t_end; t += t_stride) {
   int mt, nt;
-  band_coords(t, total_m, p.n_tiles, p.gm, mt, nt);
-  const TileInfo ti = tile_rows<BM>(p, s_pre, mt);
+  const TileInfo ti = band_tile<BM>(p, s_pre, t, p.n_tiles, p.gm, mt, nt);
 
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
@@ -277,8 +279,7 @@ __global__ void __launch_bounds__(WM * WN * 64)
   xcd_share(total_m * p.n_tiles, t_first, t_end, t_stride);
   for (int t = t_first; t < t_end; t += t_stride) {
     int mt, nt;
-    band_coords(t, total_m, p.n_tiles, p.gm, mt, nt);
-    const TileInfo ti = tile_rows<BM>(p, s_pre, mt);
+    const TileInfo ti = band_tile<BM>(p, s_pre, t, p.n_tiles, p.gm, mt, nt);
     Tile::run(p, ti, nt, smem, nullptr);
   }
 }
@@ -297,8 +298,7 @@ __global__ void __launch_bounds__(256) grouped_gemm_f32(GemmArgs p) {
   xcd_share(total_m * p.n_tiles, t_first, t_end, t_stride);
   for (int t = t_first; t < t_end; t += t_stride) {
   int mt, nt;
-  band_coords(t, total_m, p.n_tiles, p.gm, mt, nt);
-  const TileInfo ti = tile_rows<BM>(p, s_pre, mt);
+  const TileInfo ti = band_tile<BM>(p, s_pre, t, p.n_tiles, p.gm, mt, nt);
 
   const int tid = (int)threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
@@ -469,11 +469,11 @@ int pick_tile(GemmArgs a, int max_rows, hipStream_t s) {
     }
   }
   if (WK == W_SAME) {
-    if (best == 0) return run_dma<DT, EPI, 256, 256, 2, 2>(a, max_rows, 4, s);
-    return run_dma<DT, EPI, 128, 256, 2, 2>(a, max_rows, 4, s);
+    if (best == 0) return run_dma<DT, EPI, 256, 256, 2, 2>(a, max_rows, 8, s);
+    return run_dma<DT, EPI, 128, 256, 2, 2>(a, max_rows, 8, s);
   }
-  if (best == 0) return run_mfma<DT, WK, EPI, 256, 256, 2, 2>(a, max_rows, 4, s);
-  return run_mfma<DT, WK, EPI, 128, 256, 2, 2>(a, max_rows, 4, s);
+  if (best == 0) return run_mfma<DT, WK, EPI, 256, 256, 2, 2>(a, max_rows, 8, s);
+  return run_mfma<DT, WK, EPI, 128, 256, 2, 2>(a, max_rows, 8, s);
 }
 
 template <int EPI>

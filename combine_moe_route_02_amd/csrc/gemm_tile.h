@@ -51,47 +51,54 @@ __device__ __forceinline__ int build_mtile_table(const GemmArgs& p, int* s_pre, 
   return carry;
 }
 
-// m-tile index -> group and row range (binary search in the prefix table).
+// Tile t of the expert-band order -> its m-tile, n-tile and rows.  The tiles
+// of one group (its m-tiles x all n-tiles) are consecutive, so every weight
+// tile of a group is used by all of that group's m-tiles close together in
+// time: one HBM read, L2 hits after.  A group with more than gm m-tiles is cut
+// into bands of gm m-tiles; inside a band the m-tile index runs fastest.
 template <int BM>
-__device__ __forceinline__ TileInfo tile_rows(const GemmArgs& p, const int* s_pre, int mt) {
+__device__ __forceinline__ TileInfo band_tile(const GemmArgs& p, const int* s_pre, int t,
+                                              int n_tiles, int gm, int& mt, int& nt) {
+  int g = 0;
+  if (p.offsets != nullptr) {
+    int lo = 0, hi = p.n_groups - 1;  // first g whose tiles end after t
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pre[mid] * n_tiles > t) hi = mid; else lo = mid + 1;
+    }
+    g = lo;
+  }
+  const int m_before = g > 0 ? s_pre[g - 1] : 0;
+  const int mt_g = s_pre[g] - m_before;
+  const int w = t - m_before * n_tiles;
+  const int full = mt_g / gm;
+  const int per_band = gm * n_tiles;
+  const int band = w / per_band;
+  int mloc;
+  if (band < full) {
+    const int r = w - band * per_band;
+    nt = r / gm;
+    mloc = band * gm + r % gm;
+  } else {
+    const int gl = mt_g - full * gm;
+    const int r = w - full * per_band;
+    nt = r / gl;
+    mloc = full * gm + r % gl;
+  }
+  mt = m_before + mloc;
   TileInfo ti;
   if (p.offsets == nullptr) {
     ti.g = 0;
     ti.r0 = mt * BM;
     ti.r1 = p.dense_M;
     ti.base = 0;
-    return ti;
-  }
-  int lo = 0, hi = p.n_groups - 1;   // first g with s_pre[g] > mt
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (s_pre[mid] > mt) hi = mid; else lo = mid + 1;
-  }
-  const int before = lo > 0 ? s_pre[lo - 1] : 0;
-  ti.g = lo;
-  ti.base = p.offsets[p.e_begin];
-  ti.r0 = p.offsets[p.e_begin + lo] + (mt - before) * BM;
-  ti.r1 = p.offsets[p.e_begin + lo + 1];
-  return ti;
-}
-
-// Tile t of the band order -> (m-tile, n-tile).  Bands hold gm m-tiles (the
-// last band may hold fewer); inside a band the m-tile index runs fastest.
-__device__ __forceinline__ void band_coords(int t, int total_m, int n_tiles, int gm,
-                                            int& mt, int& nt) {
-  const int full = total_m / gm;
-  const int per_band = gm * n_tiles;
-  const int band = t / per_band;
-  if (band < full) {
-    const int w = t - band * per_band;
-    nt = w / gm;
-    mt = band * gm + w % gm;
   } else {
-    const int gl = total_m - full * gm;
-    const int w = t - full * per_band;
-    nt = w / gl;
-    mt = full * gm + w % gl;
+    ti.g = g;
+    ti.base = p.offsets[p.e_begin];
+    ti.r0 = p.offsets[p.e_begin + g] + mloc * BM;
+    ti.r1 = p.offsets[p.e_begin + g + 1];
   }
+  return ti;
 }
 
 // The share of tiles [lo, hi) of this workgroup's XCD and its stride.  The
