@@ -339,6 +339,9 @@ int fused_impl(const void* x, const int32_t* offsets, const int32_t* slot_of,
   f.ws = (int*)ws;
   f.max_mt = max_mtiles(T, k, E);
   if ((2 * I) % 256 || H % 256) return MOE_ERR_UNSUPPORTED;
+  // the GEMM tiles address x rows and one expert's weights with 32-bit offsets
+  if ((long long)T * H * 2 >= (1ll << 32) || 2ll * I * H * 2 >= (1ll << 32))
+    return MOE_ERR_UNSUPPORTED;
   const double avg = (double)max_rows / (n_groups > 0 ? n_groups : 1);
   const bool big = avg >= 384.0;
   if (act_dtype == MOE_DTYPE_BF16) {

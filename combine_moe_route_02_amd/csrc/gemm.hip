@@ -426,7 +426,9 @@ int run_mfma(GemmArgs a, int max_rows, int gm, hipStream_t s) {
 
 template <int DT, int EPI, int BM, int BN, int WM, int WN>
 int run_dma(GemmArgs a, int max_rows, int gm, hipStream_t s) {
-  if (a.Nb % BN || a.K % 32) return MOE_ERR_UNSUPPORTED;
+  if (a.Nb % BN || a.K % 64) return MOE_ERR_UNSUPPORTED;
+  // per-lane DMA offsets are 32-bit: one group's weight matrix must span < 4 GiB
+  if ((long long)a.Nb * a.ldb * 2 >= (1ll << 32)) return MOE_ERR_UNSUPPORTED;
   if (a.offsets && a.n_groups > 1024) return MOE_ERR_UNSUPPORTED;
   auto kern = grouped_gemm_dma<DT, EPI, BM, BN, WM, WN>;
   const dim3 grid = persistent_grid(kern, WM * WN * 64, a, max_rows, BM, BN, gm);

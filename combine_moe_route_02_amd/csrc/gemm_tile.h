@@ -141,23 +141,30 @@ __device__ __forceinline__ float gelu_erf(float a) {
 }
 
 // ---------------------------------------------------------------------------
-// 16-bit weights: direct-to-LDS staging (global_load_lds_dwordx4), BK = 32,
-// four LDS stages, loads issued three k-steps ahead.
+// 16-bit weights: direct-to-LDS staging (global_load_lds_dwordx4), BK = 64,
+// two LDS stages; the next stage loads during the whole current k-step.
 //
-// Stage layout: rows of 64 bytes (32 values); 16-byte chunk kc of row r sits
-// at chunk kc ^ dma_swz(r), so the 32 rows an MFMA operand read touches
-// (same logical chunk) spread over all bank groups.  One wave instruction
-// fills one 1 KB block (16 rows): lane p writes row p/4, physical chunk p%4,
-// and fetches the logical chunk that belongs there.  The hardware performs
-// these LDS writes; the wave only tracks them with vmcnt, so each k-step
-// waits for its own stage's loads (vmcnt = loads issued after it) and then a
-// barrier makes every wave's loads visible.
+// Stage layout: rows of 128 bytes (64 values, one full cache line of a
+// K-contiguous row); 16-byte chunk kc of row r sits at chunk kc ^ dma_swz(r),
+// so the 32 rows an MFMA operand read touches (same logical chunk) spread
+// over all bank groups.  One wave instruction fills one 1 KB block (8 rows):
+// lane p writes row p/8, physical chunk p%8, and fetches the logical chunk
+// that belongs there.  Whole 128-byte lines per row matter: the same bytes
+// fetched as 64-byte halves of twice as many lines take twice as many L2
+// requests, and the request rate, not the byte rate, bounds a CU's copies
+// when every k-step touches hundreds of rows.  The hardware performs the LDS
+// writes; the wave only tracks them with vmcnt, so a k-step waits for its
+// stage's loads and then a barrier makes every wave's loads visible.
 // ---------------------------------------------------------------------------
 
-// LDS chunk swizzle of a 64-byte row: conflict-free for the 32 rows of an
+// LDS chunk swizzle of a 128-byte row: conflict-free for the 32 rows of an
 // MFMA operand read whether the LDS serves 8 lanes x 16 B (32 banks) or
 // 16 lanes x 16 B (64 banks) per cycle.
-__device__ __forceinline__ int dma_swz(int row) { return ((row >> 2) & 3) ^ (row & 2); }
+__device__ __forceinline__ int dma_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+#ifndef MOE_SKEW
+#define MOE_SKEW(nt, nk) ((((nt) & 7) * 2) % (nk))
+#endif
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -172,16 +179,40 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// One wave-wide 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4):
-// lane l's 16 bytes land at LDS byte address lds_base + 16 * l.  Issued
-// from asm so that the compiler does not add its own conservative vmcnt(0)
-// before every later LDS read; the instruction writes no VGPR, and the
-// kernel's counted vmcnt waits order it before the reads of its stage.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+// One wave-wide 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4,
+// scalar-base form): lane l reads base + voff_l and its 16 bytes land at LDS
+// byte address lds_base + 16 * l.  The base is wave-uniform (SGPRs) and the
+// per-lane 32-bit offsets stay fixed for a tile, so advancing a k-step is a
+// scalar add and issuing a copy costs no vector instruction (a vector address
+// computed per copy would have to wait for the previous copy to read its
+// address registers).  Issued from asm so that the compiler does not add its
+// own conservative vmcnt(0) before every later LDS read; the instruction
+// writes no VGPR, and the kernel's counted vmcnt waits order it before the
+// reads of its stage.
+__device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(g), "s"(lds_base)
+               : "v"(voff), "s"(base), "s"(lds_base)
                : "memory");
+}
+
+// L2 prefetch: one dword of each lane's line is copied to a scratch LDS
+// slot that nothing reads (lane l writes lds_base + 4 * l), which brings the
+// lines into L2 ahead of their stage's copy.  Counted by vmcnt like dma16.
+__device__ __forceinline__ void prefetch4(const char* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds_base)
+               : "memory");
+}
+
+// A pointer the compiler cannot prove uniform, made uniform (its value is
+// the same in every lane by construction).
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -192,22 +223,27 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // stage layout above).  A rows come from p.A at row r - a_sub, or, with
 // a_gather, at row a_gather[r] (the fused kernel reads token rows of x
 // through the layout map instead of a gathered copy).  smem must hold
-// SMEM bytes; all threads of the block call it.
+// SMEM bytes; all threads of the block call it.  K must be a multiple of 64.
 template <int DT, int EPI, int BM, int BN, int WM, int WN>
 struct DmaTile {
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * 64;
-  static constexpr int BK = 32, NS = 4;
+  static constexpr int BK = 64, NS = 2;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int TM = WTM / 32, TN = WTN / 32;
-  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  static constexpr int ROWB = BK * 2;  // bytes per staged row
+  static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int A_BLK = BM / 16, B_BLK = BN / 16;
-  static constexpr int BPW = (A_BLK + B_BLK) / NW;  // DMA blocks per wave
-  static constexpr int SMEM = NS * STAGE;
-  static_assert((A_BLK + B_BLK) % NW == 0, "blocks per wave");
+  static constexpr int A_BLK = BM / 8, B_BLK = BN / 8;  // 1 KB blocks of 8 rows
+  static constexpr int BPW = (A_BLK + B_BLK) / NW;       // DMA blocks per wave
+  static constexpr int NPF = (BM + BN + 64 * NW - 1) / (64 * NW);  // prefetches per wave
+  static constexpr int PF_OFS = NS * STAGE;                         // scratch slots
+  static constexpr int SMEM = NS * STAGE + NW * 256;
+  static_assert(A_BLK % NW == 0 && B_BLK % NW == 0, "blocks per wave");
   static_assert(TM >= 1 && TN >= 1, "tile");
   static_assert(EPI != EPI_SWIGLU || (TN % 2) == 0, "swiglu pairs");
+  static_assert(BPW + 2 * NPF < 64, "vmcnt range");
+  static_assert(BM % 64 == 0, "prefetch rows split at the A/B boundary per wave");
 
   __device__ static __forceinline__ void run(const GemmArgs& p, const TileInfo& ti, int nt,
                                              char* smem, const int32_t* a_gather) {
@@ -218,26 +254,38 @@ struct DmaTile {
     const int wm = wave / WN, wn = wave % WN;
     const int lrow = lane & 31;
     const int khalf = lane >> 5;
-    const int prow = lane >> 2, pchunk = lane & 3;  // DMA lane -> (row, chunk)
-    // MFMA operand read: logical chunk 2s + khalf of a row whose swizzle is
-    // that of lrow (tile rows start at multiples of 32).
-    const int sw0 = ((0 + khalf) ^ dma_swz(lrow)) << 4;
-    const int sw1 = ((2 + khalf) ^ dma_swz(lrow)) << 4;
+    const int prow = lane >> 3, pchunk = lane & 7;  // DMA lane -> (row, chunk)
+    // MFMA operand read of k16 substep s: logical chunk 2s + khalf of a row
+    // whose swizzle is that of lrow (tile rows start at multiples of 32).
+    int swo[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) swo[s4] = ((2 * s4 + khalf) ^ dma_swz(lrow)) << 4;
 
     const int a_sub = p.a_local ? ti.base : 0;
     const int c_sub = p.c_local ? ti.base : 0;
     const int n0 = nt * BN;
     const int n0h = nt * (BN / 2);
 
-    // Source of each of this wave's DMA blocks (fixed for the tile; the
-    // k-step adds BK * 2 bytes).
-    const char* src[BPW];
+    // Sources of this wave's DMA blocks: a uniform base per operand and a
+    // per-lane 32-bit byte offset, both fixed for the tile; a k-step moves the
+    // bases.  A: rows relative to the tile's first row (or token rows of x
+    // through a_gather); B: rows of this group's weight matrix.  Blocks
+    // j < JA are A blocks (block q = wave + NW * j).
+    constexpr int JA = A_BLK / NW;
+    int base_row = 0;
+    if (!a_gather) {
+      base_row = ti.r0 - a_sub;
+      if (p.a_local && base_row > p.a_rows - 1) base_row = p.a_rows - 1;
+    }
+    const char* a_tile = uniform_ptr((const char*)p.A + (long long)base_row * p.lda * 2);
+    const char* b_tile = uniform_ptr((const char*)p.B + (long long)ti.g * p.strideB * 2);
+    uint32_t voff[BPW];
     int ldsoff[BPW];
 #pragma unroll
     for (int j = 0; j < BPW; ++j) {
       const int q = wave + NW * j;
-      if (q < A_BLK) {
-        const int row = 16 * q + prow;
+      if (j < JA) {
+        const int row = 8 * q + prow;
         const int kc = pchunk ^ dma_swz(row);
         int grow = ti.r0 + row;
         grow = grow < ti.r1 ? grow : ti.r1 - 1;
@@ -248,10 +296,10 @@ struct DmaTile {
           arow = grow - a_sub;
           if (p.a_local && arow >= p.a_rows) arow = p.a_rows - 1;
         }
-        src[j] = (const char*)p.A + ((long long)arow * p.lda) * 2 + kc * 16;
+        voff[j] = (uint32_t)(arow - base_row) * (uint32_t)(p.lda * 2) + (uint32_t)(kc * 16);
         ldsoff[j] = q * 1024;
       } else {
-        const int row = 16 * (q - A_BLK) + prow;
+        const int row = 8 * (q - A_BLK) + prow;
         const int kc = pchunk ^ dma_swz(row);
         int n;
         if (EPI == EPI_SWIGLU) {
@@ -260,9 +308,42 @@ struct DmaTile {
         } else {
           n = n0 + row;
         }
-        src[j] = (const char*)p.B + ((long long)ti.g * p.strideB + (long long)n * p.ldb) * 2 +
-                 kc * 16;
+        voff[j] = (uint32_t)n * (uint32_t)(p.ldb * 2) + (uint32_t)(kc * 16);
         ldsoff[j] = A_BYTES + (q - A_BLK) * 1024;
+      }
+    }
+
+    // L2 prefetch rows: instruction i of this wave covers rows
+    // (i * NW + wave) * 64 + lane of [A rows | B rows] (past the end: the last
+    // B row again); each wave's 64 rows lie on one side of the boundary.
+    uint32_t pfoff[NPF];
+    bool pf_a[NPF];
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {
+      const int r = (i * NW + wave) * 64 + lane;
+      pf_a[i] = (i * NW + wave) * 64 < BM;
+      if (pf_a[i]) {
+        int grow = ti.r0 + r;
+        grow = grow < ti.r1 ? grow : ti.r1 - 1;
+        int arow;
+        if (a_gather) {
+          arow = a_gather[grow];
+        } else {
+          arow = grow - a_sub;
+          if (p.a_local && arow >= p.a_rows) arow = p.a_rows - 1;
+        }
+        pfoff[i] = (uint32_t)(arow - base_row) * (uint32_t)(p.lda * 2);
+      } else {
+        int row = r - BM;
+        row = row < BN ? row : BN - 1;
+        int n;
+        if (EPI == EPI_SWIGLU) {
+          const int gi = row >> 5;
+          n = ((gi & 1) ? p.I : 0) + n0h + (gi >> 1) * 32 + (row & 31);
+        } else {
+          n = n0 + row;
+        }
+        pfoff[i] = (uint32_t)n * (uint32_t)(p.ldb * 2);
       }
     }
 
@@ -276,16 +357,23 @@ struct DmaTile {
 
     const int nk = p.K / BK;
     const uint32_t lds0 = lds_addr(smem);
+    // k-order rotation: tiles of different n-tiles start at different k so
+    // that the workgroups of a band (which run in lockstep) do not all read
+    // the same column of power-of-two-pitched rows at once, which
+    // concentrates the traffic on a few memory channels.  Tiles sharing an
+    // n-tile share the rotation (and so their weight reads).
+    const int skew = MOE_SKEW(nt, nk);
+#define MOE_KOFS(st) ((((st) + skew) < nk ? (st) + skew : (st) + skew - nk) * ROWB)
 
-// Fragments of one k16 substep (sw = sw0 or sw1) of a stage into FA/FB.
-#define MOE_READ_HALF(stage, sw, FA, FB)                                           \
+// Fragments of k16 substep s4 of a stage into FA/FB.
+#define MOE_READ(stage, s4, FA, FB)                                                \
 do {                                                                             \
     const char* As_ = smem + (stage) * STAGE;                                      \
     const char* Bs_ = As_ + A_BYTES;                                               \
     _Pragma("unroll") for (int i = 0; i < TM; ++i)                                 \
-      FA[i] = *(const V*)(As_ + (wm * WTM + i * 32 + lrow) * 64 + (sw));           \
+      FA[i] = *(const V*)(As_ + (wm * WTM + i * 32 + lrow) * ROWB + swo[s4]);      \
     _Pragma("unroll") for (int j = 0; j < TN; ++j)                                 \
-      FB[j] = *(const V*)(Bs_ + (wn * WTN + j * 32 + lrow) * 64 + (sw));           \
+      FB[j] = *(const V*)(Bs_ + (wn * WTN + j * 32 + lrow) * ROWB + swo[s4]);      \
 } while (0)
 #define MOE_MFMAS(FA, FB)                                                          \
 do {                                                                             \
@@ -293,99 +381,145 @@ do {                                                                            
     _Pragma("unroll") for (int j = 0; j < TN; ++j)                                 \
       acc[i][j] = MfmaOp<DT>::run(FA[i], FB[j], acc[i][j]);                        \
 } while (0)
-// A stage becomes readable: wait until at most `n_after` (0..3) later
-// stages of this wave's copies are still in flight, finish this wave's LDS
-// reads, then a barrier covers the other waves' copies and reads.
-#define MOE_STAGE_READY(n_after)                                                   \
+// The next stage becomes readable: this wave's copies of it are done (only
+// the n_pf prefetch groups issued after them may be in flight), its LDS
+// reads are done, and a barrier covers the other waves' copies and reads.
+#define MOE_STAGE_READY(n_pf)                                                      \
 do {                                                                             \
-    const int na_ = (n_after);                                                     \
-    if (na_ >= 3) wait_vmcnt<3 * BPW>();                                           \
-    else if (na_ == 2) wait_vmcnt<2 * BPW>();                                      \
-    else if (na_ == 1) wait_vmcnt<BPW>();                                          \
-    else wait_vmcnt<0>();                                                          \
-    __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x7 << 4) | ((0x3F >> 4) << 14)); \
+    MOE_WAIT_STAGE(n_pf);                                                          \
+    __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x7 << 4) | ((0x3F >> 4) << 14));  \
     __builtin_amdgcn_s_barrier();                                                  \
     asm volatile("" ::: "memory");                                                 \
 } while (0)
 #define MOE_ISSUE(st)                                                              \
 do {                                                                             \
     const uint32_t dst_ = lds0 + ((st) % NS) * STAGE;                              \
+    const char* ak_ = a_tile + MOE_KOFS(st);                                       \
+    const char* bk_ = b_tile + MOE_KOFS(st);                                       \
     _Pragma("unroll") for (int j = 0; j < BPW; ++j)                                \
-      dma16(src[j] + (st) * BK * 2, dst_ + ldsoff[j]);                             \
+      dma16(j < JA ? ak_ : bk_, voff[j], dst_ + ldsoff[j]);                        \
 } while (0)
-
-    static_assert(NS == 4, "wait counts assume four stages");
-    static_assert(3 * BPW < 64, "vmcnt range");
-    V xa[TM], xb[TN], ya[TM], yb[TN];
-    // Every wave is done with the previous tile's stages: fill all four.
-    lds_barrier();
-#pragma unroll
-    for (int st = 0; st < NS; ++st)
-      if (st < nk) MOE_ISSUE(st);
-    MOE_STAGE_READY(nk - 1 < 3 ? nk - 1 : 3);  // stage 0; stages 1..3 may be in flight
-    MOE_READ_HALF(0, sw0, xa, xb);
-
-    // Loop invariant at the top of iteration kt: stage kt is visible, its
-    // first k16 half is in (xa, xb) (reads possibly in flight), stages up to
-    // kt+3 have been issued.  The second half is read during the first
-    // half's MFMAs.  Then stage kt+1 is made visible (stages kt+2, kt+3 may
-    // stay in flight), stage kt's buffer, now fully read by every wave, is
-    // refilled with stage kt+4, and stage kt+1's first half is read during
-    // the second half's MFMAs.  The steady-state body is straight-line so
-    // the compiler's own LDS wait counts stay exact; the last iterations
-    // (no refill, full drain) are peeled.
-    int kt = 0;
-    // sched_barrier(0) keeps each phase's LDS reads ahead of the MFMAs that
-    // overlap them (the scheduler would otherwise sink each read to its use).
+#define MOE_PREFETCH(st)                                                           \
+do {                                                                             \
+    const uint32_t pdst_ = lds0 + PF_OFS + wave * 256;                             \
+    _Pragma("unroll") for (int i = 0; i < NPF; ++i)                                \
+      prefetch4((pf_a[i] ? a_tile : b_tile) + MOE_KOFS(st), pfoff[i], pdst_);      \
+} while (0)
+// Wait until at most n_pf prefetch groups (issued after the stage's copies)
+// are in flight.
+#define MOE_WAIT_STAGE(n_pf)                                                       \
+do {                                                                             \
+    const int np_ = (n_pf);                                                        \
+    if (np_ >= 2) wait_vmcnt<2 * NPF>();                                           \
+    else if (np_ == 1) wait_vmcnt<NPF>();                                          \
+    else wait_vmcnt<0>();                                                          \
+} while (0)
+// sched_barrier(0) keeps each phase's LDS reads ahead of the MFMAs that
+// overlap them (the scheduler would otherwise sink each read to its use).
 #define MOE_PHASE() __builtin_amdgcn_sched_barrier(0)
-    for (; kt < nk - NS; ++kt) {
-      MOE_READ_HALF(kt % NS, sw1, ya, yb);
+
+    V xa[TM], xb[TN], ya[TM], yb[TN];
+    // Every wave is done with the previous tile's stages: fill both.
+    lds_barrier();
+    MOE_ISSUE(0);
+    if (nk > 1) MOE_ISSUE(1);
+    if (nk > 2) MOE_PREFETCH(2);
+    if (nk > 3) MOE_PREFETCH(3);
+    // stage 0 landed; stage 1 and the prefetches may be in flight
+    {
+      const int npf0 = (nk > 2) + (nk > 3);
+      if (nk <= 1) wait_vmcnt<0>();
+      else if (npf0 == 0) wait_vmcnt<BPW>();
+      else if (npf0 == 1) wait_vmcnt<BPW + NPF>();
+      else wait_vmcnt<BPW + 2 * NPF>();
+    }
+    __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x7 << 4) | ((0x3F >> 4) << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    MOE_READ(0, 0, xa, xb);
+
+    // Loop invariant at the top of k-step kt: stage kt is visible and its
+    // substep 0 is in (xa, xb) (reads possibly in flight); stage kt+1 has
+    // been issued.  Substeps 1..3 are read one substep ahead of their
+    // MFMAs.  During substep 3 the next stage is made visible, its substep 0
+    // read, and stage kt's buffer (read by every wave by then) refilled
+    // with stage kt+2, one copy per MFMA so the issue slots overlap the
+    // matrix pipe.  The body is straight-line so the compiler's own LDS
+    // wait counts stay exact.
+    int kt = 0;
+    for (; kt < nk - 2; ++kt) {
+      const int st = kt & 1;
+      MOE_READ(st, 1, ya, yb);
       MOE_PHASE();
       MOE_MFMAS(xa, xb);
       MOE_PHASE();
-      MOE_STAGE_READY(2);
-      MOE_READ_HALF((kt + 1) % NS, sw0, xa, xb);
+      MOE_READ(st, 2, xa, xb);
+      MOE_PHASE();
+      MOE_MFMAS(ya, yb);
+      MOE_PHASE();
+      MOE_READ(st, 3, ya, yb);
+      MOE_PHASE();
+      MOE_MFMAS(xa, xb);
+      MOE_PHASE();
+      // prefetch groups issued after stage kt+1's copies: the prologue's two
+      // for kt = 0, else the one issued with them (if any)
+      MOE_STAGE_READY(kt == 0 ? (nk > 2) + (nk > 3) : (kt + 3 < nk));
+      MOE_READ(st ^ 1, 0, xa, xb);
       MOE_PHASE();
       {
-        // Refill stage kt's buffer with stage kt+NS, one copy every few
-        // MFMAs so the issue slots overlap the matrix pipe.
-        const uint32_t dst_ = lds0 + ((kt + NS) % NS) * STAGE;
-        const int kofs_ = (kt + NS) * BK * 2;
+        const uint32_t dst_ = lds0 + st * STAGE;
+        const int kofs_ = MOE_KOFS(kt + 2);
+        const char* ak_ = a_tile + kofs_;
+        const char* bk_ = b_tile + kofs_;
         constexpr int MF = TM * TN;
         constexpr int EVERY = MF / BPW > 0 ? MF / BPW : 1;
 #pragma unroll
         for (int q = 0; q < MF; ++q) {
           acc[q / TN][q % TN] = MfmaOp<DT>::run(ya[q / TN], yb[q % TN], acc[q / TN][q % TN]);
-          if ((q % EVERY) == EVERY - 1 && q / EVERY < BPW) {
-            dma16(src[q / EVERY] + kofs_, dst_ + ldsoff[q / EVERY]);
-            MOE_PHASE();
-          }
-        }
 #pragma unroll
-        for (int j = MF / EVERY; j < BPW; ++j) dma16(src[j] + kofs_, dst_ + ldsoff[j]);
+          for (int r = 0; r < (BPW + MF - 1) / MF; ++r) {
+            const int j = (q / EVERY) * ((BPW + MF - 1) / MF) + r;
+            if ((q % EVERY) == EVERY - 1 && j < BPW) {
+              dma16(j < JA ? ak_ : bk_, voff[j], dst_ + ldsoff[j]);
+            }
+          }
+          MOE_PHASE();
+        }
       }
+      if (kt + 4 < nk) MOE_PREFETCH(kt + 4);
       MOE_PHASE();
     }
-    for (; kt < nk - 1; ++kt) {
-      MOE_READ_HALF(kt % NS, sw1, ya, yb);
+    // Last two k-steps: no refill.
+    for (; kt < nk; ++kt) {
+      const int st = kt & 1;
+      MOE_READ(st, 1, ya, yb);
       MOE_PHASE();
       MOE_MFMAS(xa, xb);
       MOE_PHASE();
-      MOE_STAGE_READY(0);
-      MOE_READ_HALF((kt + 1) % NS, sw0, xa, xb);
+      MOE_READ(st, 2, xa, xb);
       MOE_PHASE();
       MOE_MFMAS(ya, yb);
       MOE_PHASE();
+      MOE_READ(st, 3, ya, yb);
+      MOE_PHASE();
+      MOE_MFMAS(xa, xb);
+      MOE_PHASE();
+      if (kt + 1 < nk) {
+        MOE_STAGE_READY(kt == 0 ? (nk > 2) + (nk > 3) : (kt + 3 < nk));
+        MOE_READ(st ^ 1, 0, xa, xb);
+        MOE_PHASE();
+      }
+      MOE_MFMAS(ya, yb);
+      MOE_PHASE();
     }
-    MOE_READ_HALF(kt % NS, sw1, ya, yb);
-    MOE_PHASE();
-    MOE_MFMAS(xa, xb);
-    MOE_MFMAS(ya, yb);
 #undef MOE_PHASE
-#undef MOE_READ_HALF
+#undef MOE_READ
 #undef MOE_MFMAS
 #undef MOE_STAGE_READY
 #undef MOE_ISSUE
+#undef MOE_PREFETCH
+#undef MOE_WAIT_STAGE
+#undef MOE_KOFS
 
     // Epilogue (32x32 f32 layout: lane l -> column l % 32, rows
     // 8*(v/4) + 4*(l/32) + v%4).
