@@ -230,9 +230,16 @@ def main():
         achieved = flops1 / (gemm1_ms * 1e9)
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_MFMA_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4)}
-    roof["kernel"] = ("fused_layer_kernel (GEMM-1 + SwiGLU + GEMM-2 + combine, moe_layer_fused)"
-                      if args.fused else
-                      "grouped_gemm_dma (GEMM-1 + SwiGLU, moe_expert_ffn_up)")
+    n_loc = max(1, e1 - e0)
+    if args.fused:
+        kname = "fused_layer_kernel (GEMM-1 + SwiGLU + GEMM-2 + combine, moe_layer_fused)"
+    elif cfg.w_dtype == "e4m3":
+        small_m = lay.spec.max_rows / n_loc <= 48
+        kname = ("grouped_gemm_fp8s" if small_m else "grouped_gemm_mfma") + \
+            " (GEMM-1 + SwiGLU, fp8 weights, moe_expert_ffn_up)"
+    else:
+        kname = "grouped_gemm_dma (GEMM-1 + SwiGLU, moe_expert_ffn_up)"
+    roof["kernel"] = kname
     roof["avg_launch_ms"] = round(gemm1_ms, 5)
     roof["traffic"] = load_traffic("gemm1", cfg.name)
 
@@ -303,7 +310,7 @@ def pmc_summary(fetch_csv, write_csv, out_path, calib_mib, workload):
         if "grouped_gemm" not in name or "<" not in name:
             return False
         targs = [a.strip() for a in name.split("<", 1)[1].split(">", 1)[0].split(",")]
-        epi = targs[1] if "grouped_gemm_dma" in name else targs[2]  # SwiGLU epilogue = 1
+        epi = targs[2] if "grouped_gemm_mfma" in name else targs[1]  # SwiGLU epilogue = 1
         return epi == "1"
     gemm = [k for k in fetch if is_gemm1(k)]
     lines = [f"# HBM traffic per launch of the GEMM-1 (+SwiGLU) kernel, workload {workload}",

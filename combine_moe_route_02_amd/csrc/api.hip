@@ -53,11 +53,7 @@ int moe_route(const void* x, const void* w_router, int act_dtype, const float* b
   if (!(inv_temperature >= 0.0f) || inv_temperature > 3.0e38f) return MOE_ERR_ARG;
   if (T == 0) return MOE_OK;
   if (!logits || !topk_idx || !topk_w) return MOE_ERR_ARG;
-  if (w_router) {
-    if (!x || H < 1 || H % 8) return MOE_ERR_ARG;
-    const bool mfma = act_dtype != MOE_DTYPE_F32 && E % 128 == 0 && H % 64 == 0;
-    if (!mfma && E > 128) return MOE_ERR_UNSUPPORTED;
-  }
+  if (w_router && (!x || H < 1 || H % 8)) return MOE_ERR_ARG;
   return route_impl(x, w_router, act_dtype, bias, T, H, E, k, gate, renorm,
                     inv_temperature, logits, topk_idx, topk_w, stream);
 }

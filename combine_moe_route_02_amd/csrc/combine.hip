@@ -6,10 +6,12 @@
 // reverse: row slot_of[t][j] of y_perm holds the j-th expert's output for t
 // (DySHARP page, section 3.1 item 3).
 //
-// One wave per token: the token's k row numbers and weights are wave-uniform
-// (scalar loads); each lane owns 16-byte chunks of the row, accumulates the
-// k products in float32 in pick order and rounds once.  The k loads of a
-// chunk are independent, so each lane keeps k x 16 bytes in flight.
+// One wave per token and column slice (a small batch is cut into slices of
+// the row so that enough waves are in flight): the token's k row numbers and
+// weights are wave-uniform (scalar loads); each lane owns 16-byte chunks of
+// the slice, accumulates the k products in float32 in pick order and rounds
+// once.  The k loads of a chunk are independent, so each lane keeps k x 16
+// bytes in flight.
 
 #include "moe_internal.h"
 
@@ -18,7 +20,7 @@ namespace moe {
 template <int DT, int KMAX>
 __global__ void __launch_bounds__(256)
     combine_kernel(const uint4* __restrict__ y_perm, const int32_t* __restrict__ slot_of,
-                   const float* __restrict__ topk_w, int T, int k, int nch,
+                   const float* __restrict__ topk_w, int T, int k, int nch, int cps,
                    uint4* __restrict__ out) {
   constexpr int EPC = DT == MOE_DTYPE_F32 ? 4 : 8;  // elements per chunk
   const int t = __builtin_amdgcn_readfirstlane(
@@ -37,7 +39,9 @@ __global__ void __launch_bounds__(256)
     }
   }
   uint4* dst = out + (long long)t * nch;
-  for (int c = lane; c < nch; c += 64) {
+  const int c0 = (int)blockIdx.y * cps;
+  const int c1 = min(nch, c0 + cps);
+  for (int c = c0 + lane; c < c1; c += 64) {
     uint4 q[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
@@ -73,10 +77,12 @@ namespace {
 template <int DT>
 int launch_combine_dt(const void* y_perm, const int32_t* slot_of, const float* w,
                       int T, int k, int nch, void* out, hipStream_t s) {
-  const dim3 grid((T + 3) / 4), block(256);
+  int slices, cps;
+  row_slices(T, nch, slices, cps);
+  const dim3 grid((T + 3) / 4, slices), block(256);
 #define MOE_COMBINE(KM)                                                        \
   hipLaunchKernelGGL((combine_kernel<DT, KM>), grid, block, 0, s,             \
-                     (const uint4*)y_perm, slot_of, w, T, k, nch, (uint4*)out)
+                     (const uint4*)y_perm, slot_of, w, T, k, nch, cps, (uint4*)out)
   if (k <= 1) MOE_COMBINE(1);
   else if (k <= 2) MOE_COMBINE(2);
   else if (k <= 4) MOE_COMBINE(4);

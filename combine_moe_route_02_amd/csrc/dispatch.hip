@@ -11,14 +11,18 @@
 // communication kernels).
 //
 // Kernels (tile = 256 tokens = 4 waves):
+//   layout_one_tile  hist + scan + slots in one block for T <= 256
 //   hist    per-tile expert histogram (LDS integer atomics: exact counts)
 //   scan    per-expert prefix over tiles -> tile bases, counts, offsets
 //   slots   rank of each pick among earlier picks of the same expert:
-//           earlier waves via per-wave LDS histograms, earlier lanes of the
-//           same wave via ballots over the expert-id bits; no atomics decide
-//           any order, so the layout is deterministic and token-stable
-//   gather  one wave per token: each 16-byte chunk of x[t] is loaded once and
-//           stored to every local row of that token
+//           per wave and expert a 64-bit mask of the lanes that picked it
+//           (LDS atomic OR); earlier waves add their popcounts, earlier lanes
+//           of the same wave the popcount of the lanes below; no atomic
+//           decides any order, so the layout is deterministic and
+//           token-stable
+//   gather  one wave per token (and column slice, for small batches): each
+//           16-byte chunk of x[t] is loaded once and stored to every local
+//           row of that token
 
 #include "moe_internal.h"
 
@@ -86,58 +90,129 @@ __global__ void __launch_bounds__(1024)
   if (e == 0) offsets[E] = s[1023];
 }
 
-__device__ __forceinline__ uint64_t lanemask_lt() {
-  const int l = lane_id();
-  return l ? (~0ull >> (64 - l)) : 0ull;
-}
-
+// Lanes of this wave that picked expert e, as a 64-bit mask per wave and
+// expert in LDS (set with atomic OR, so the result does not depend on the
+// order of the atomics): the per-wave count of e is its popcount and the
+// rank of a pick among the wave's earlier picks of e is the popcount of the
+// lanes below it.  The k picks of a token are distinct experts.
+template <int KMAX>
 __global__ void __launch_bounds__(TILE)
     slots_kernel(const int32_t* __restrict__ idx, int T, int E, int k, int n_tiles,
-                 int nbits, const int32_t* __restrict__ tile_base,
-                 const int32_t* __restrict__ offsets, int32_t* __restrict__ slot_of,
-                 int32_t* __restrict__ row_token) {
-  extern __shared__ int wcnt[];  // [4][E] per-wave counts, then exclusive
+                 const int32_t* __restrict__ tile_base, const int32_t* __restrict__ offsets,
+                 int32_t* __restrict__ slot_of, int32_t* __restrict__ row_token) {
+  extern __shared__ uint64_t lanes_of[];  // [4][E] lane masks
+  int* wbase = (int*)(lanes_of + 4 * E);  // [4][E] exclusive prefix over waves
   const int tile = (int)blockIdx.x;
   const int wave = (int)threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < 4 * E; i += TILE) wcnt[i] = 0;
+  for (int i = threadIdx.x; i < 4 * E; i += TILE) lanes_of[i] = 0;
   __syncthreads();
   const int t = tile * TILE + (int)threadIdx.x;
   const bool valid = t < T;
-  const int32_t* p = idx + (long long)(valid ? t : 0) * k;
+  int pk[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) pk[j] = (valid && j < k) ? idx[(long long)t * k + j] : 0;
+  const uint64_t bit = 1ull << lane_id();
   if (valid)
-    for (int j = 0; j < k; ++j) atomicAdd(&wcnt[wave * E + p[j]], 1);
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (j < k) atomicOr((unsigned long long*)&lanes_of[wave * E + pk[j]], bit);
   __syncthreads();
-  // exclusive prefix over the 4 waves, per expert
   for (int e = threadIdx.x; e < E; e += TILE) {
     int run = 0;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const int c = wcnt[w * E + e];
-      wcnt[w * E + e] = run;
-      run += c;
+      wbase[w * E + e] = run;
+      run += __popcll(lanes_of[w * E + e]);
     }
   }
   __syncthreads();
-  const uint64_t lt = lanemask_lt();
-  for (int j = 0; j < k; ++j) {
-    const int e = valid ? p[j] : -1;
-    uint64_t same = 0;  // lanes of this wave whose picks include e
-    for (int jj = 0; jj < k; ++jj) {
-      const int o = valid ? p[jj] : -1;
-      uint64_t eq = __ballot(valid);
-      for (int b = 0; b < nbits; ++b) {
-        const uint64_t ob = __ballot(valid && ((o >> b) & 1));
-        eq &= ((e >> b) & 1) ? ob : ~ob;
+  if (!valid) return;
+  const uint64_t lt = bit - 1;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j >= k) break;
+    const int e = pk[j];
+    const int r = offsets[e] + tile_base[(long long)e * n_tiles + tile] + wbase[wave * E + e] +
+                  __popcll(lanes_of[wave * E + e] & lt);
+    slot_of[(long long)t * k + j] = r;
+    row_token[r] = t;
+  }
+}
+
+// Whole layout of a batch of at most one tile (T <= 256, a decode batch) in
+// one block: lane masks per wave and expert as in slots_kernel, counts and
+// offsets from a block scan over experts, tile base 0.
+template <int KMAX>
+__global__ void __launch_bounds__(TILE)
+    layout_one_tile_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
+                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                           int32_t* __restrict__ slot_of, int32_t* __restrict__ row_token) {
+  extern __shared__ uint64_t lanes_of[];  // [4][E] lane masks
+  int* wbase = (int*)(lanes_of + 4 * E);  // [4][E] exclusive prefix over waves
+  int* s_off = wbase + 4 * E;             // [E] offsets
+  __shared__ int s_part[TILE];
+  const int wave = (int)threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 4 * E; i += TILE) lanes_of[i] = 0;
+  __syncthreads();
+  const int t = (int)threadIdx.x;
+  const bool valid = t < T;
+  int pk[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) pk[j] = (valid && j < k) ? idx[(long long)t * k + j] : 0;
+  const uint64_t bit = 1ull << lane_id();
+  if (valid)
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (j < k) atomicOr((unsigned long long*)&lanes_of[wave * E + pk[j]], bit);
+  __syncthreads();
+  // thread i owns experts [i * per, (i + 1) * per): prefix over the 4 waves
+  // and the expert's count
+  const int per = (E + TILE - 1) / TILE;
+  int run_total = 0;
+  for (int q = 0; q < per; ++q) {
+    const int e = (int)threadIdx.x * per + q;
+    if (e < E) {
+      int run = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        wbase[w * E + e] = run;
+        run += __popcll(lanes_of[w * E + e]);
       }
-      same |= eq;
+      counts[e] = run;
+      s_off[e] = run;  // count for now
+      run_total += run;
     }
-    if (valid) {
-      const int rank = __popcll(same & lt);
-      const int r = offsets[e] + tile_base[(long long)e * n_tiles + tile] +
-                    wcnt[wave * E + e] + rank;
-      slot_of[(long long)t * k + j] = r;
-      row_token[r] = t;
+  }
+  // block scan of the per-thread totals -> exclusive base of each thread
+  s_part[threadIdx.x] = run_total;
+  __syncthreads();
+  for (int o = 1; o < TILE; o <<= 1) {
+    const int add = (int)threadIdx.x >= o ? s_part[threadIdx.x - o] : 0;
+    __syncthreads();
+    s_part[threadIdx.x] += add;
+    __syncthreads();
+  }
+  int base = s_part[threadIdx.x] - run_total;
+  for (int q = 0; q < per; ++q) {
+    const int e = (int)threadIdx.x * per + q;
+    if (e < E) {
+      const int c = s_off[e];
+      s_off[e] = base;
+      offsets[e] = base;
+      base += c;
     }
+  }
+  if (threadIdx.x == TILE - 1) offsets[E] = s_part[TILE - 1];
+  __syncthreads();
+  if (!valid) return;
+  const uint64_t lt = bit - 1;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j >= k) break;
+    const int e = pk[j];
+    const int r = s_off[e] + wbase[wave * E + e] + __popcll(lanes_of[wave * E + e] & lt);
+    slot_of[(long long)t * k + j] = r;
+    row_token[r] = t;
   }
 }
 
@@ -148,7 +223,7 @@ __global__ void __launch_bounds__(256)
     gather_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ idx,
                   const int32_t* __restrict__ slot_of, int T, int k, int e_begin,
                   int e_end, int nch /* 16-byte chunks per row */,
-                  uint4* __restrict__ x_perm) {
+                  int cps /* chunks per column slice */, uint4* __restrict__ x_perm) {
   const int t = __builtin_amdgcn_readfirstlane(
       (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)));
   if (t >= T) return;
@@ -169,9 +244,11 @@ __global__ void __launch_bounds__(256)
   }
   if (!any) return;
   const uint4* src = x + (long long)t * nch;
+  const int c0 = (int)blockIdx.y * cps;
+  const int c1 = min(nch, c0 + cps);
   constexpr int U = 4;
-  int c = lane;
-  for (; c + (U - 1) * 64 < nch; c += U * 64) {
+  int c = c0 + lane;
+  for (; c + (U - 1) * 64 < c1; c += U * 64) {
     uint4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) v[u] = src[c + u * 64];
@@ -181,7 +258,7 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
         for (int u = 0; u < U; ++u) x_perm[rows[j] + c + u * 64] = v[u];
   }
-  for (; c < nch; c += 64) {
+  for (; c < c1; c += 64) {
     const uint4 v = src[c];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
@@ -196,34 +273,49 @@ int dispatch_impl(const void* x, int act_dtype, const int32_t* idx, int T, int H
   const int n_tiles = (T + TILE - 1) / TILE;
   int32_t* tile_counts = (int32_t*)ws;
   int32_t* tile_base = tile_counts + (size_t)E * (n_tiles > 0 ? n_tiles : 1);
-  int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
-  if (n_tiles > 0) {
-    hipLaunchKernelGGL(hist_kernel, dim3(n_tiles), dim3(TILE), E * sizeof(int), s, idx,
-                       T, E, k, n_tiles, tile_counts);
-  }
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, tile_counts, E, n_tiles,
-                     tile_base, counts, offsets);
-  if (n_tiles > 0) {
-    hipLaunchKernelGGL(slots_kernel, dim3(n_tiles), dim3(TILE), 4 * E * sizeof(int), s,
-                       idx, T, E, k, n_tiles, nbits, tile_base, offsets, slot_of,
-                       row_token);
-    const int elem = act_dtype == MOE_DTYPE_F32 ? 4 : 2;
-    const int nch = H * elem / 16;
-    if (e_end > e_begin) {
-      const dim3 grid((T + 3) / 4), block(256);
-#define MOE_GATHER(KM)                                                         \
-  hipLaunchKernelGGL((gather_kernel<KM>), grid, block, 0, s, (const uint4*)x, idx, \
-                     slot_of, T, k, e_begin, e_end, nch, (uint4*)x_perm)
-      if (k <= 1) MOE_GATHER(1);
-      else if (k <= 2) MOE_GATHER(2);
-      else if (k <= 4) MOE_GATHER(4);
-      else if (k <= 8) MOE_GATHER(8);
-      else if (k <= 16) MOE_GATHER(16);
-      else MOE_GATHER(32);
-#undef MOE_GATHER
+#define MOE_BY_K(MACRO)                                                         \
+  do {                                                                          \
+    if (k <= 1) MACRO(1);                                                       \
+    else if (k <= 2) MACRO(2);                                                  \
+    else if (k <= 4) MACRO(4);                                                  \
+    else if (k <= 8) MACRO(8);                                                  \
+    else if (k <= 16) MACRO(16);                                                \
+    else MACRO(32);                                                             \
+  } while (0)
+  if (n_tiles == 1) {
+#define MOE_LAYOUT1(KM)                                                              \
+  hipLaunchKernelGGL((layout_one_tile_kernel<KM>), dim3(1), dim3(TILE), 13 * E * sizeof(int), \
+                     s, idx, T, E, k, counts, offsets, slot_of, row_token)
+    MOE_BY_K(MOE_LAYOUT1);
+#undef MOE_LAYOUT1
+  } else {
+    if (n_tiles > 0) {
+      hipLaunchKernelGGL(hist_kernel, dim3(n_tiles), dim3(TILE), E * sizeof(int), s, idx,
+                         T, E, k, n_tiles, tile_counts);
+    }
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, tile_counts, E, n_tiles,
+                       tile_base, counts, offsets);
+    if (n_tiles > 0) {
+#define MOE_SLOTS(KM)                                                                \
+  hipLaunchKernelGGL((slots_kernel<KM>), dim3(n_tiles), dim3(TILE), 12 * E * sizeof(int), s, \
+                     idx, T, E, k, n_tiles, tile_base, offsets, slot_of, row_token)
+      MOE_BY_K(MOE_SLOTS);
+#undef MOE_SLOTS
     }
   }
+  if (n_tiles > 0 && e_end > e_begin) {
+    const int elem = act_dtype == MOE_DTYPE_F32 ? 4 : 2;
+    const int nch = H * elem / 16;
+    int slices, cps;
+    row_slices(T, nch, slices, cps);
+    const dim3 grid((T + 3) / 4, slices), block(256);
+#define MOE_GATHER(KM)                                                         \
+  hipLaunchKernelGGL((gather_kernel<KM>), grid, block, 0, s, (const uint4*)x, idx, \
+                     slot_of, T, k, e_begin, e_end, nch, cps, (uint4*)x_perm)
+    MOE_BY_K(MOE_GATHER);
+#undef MOE_GATHER
+  }
+#undef MOE_BY_K
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

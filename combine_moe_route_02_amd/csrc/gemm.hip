@@ -267,6 +267,202 @@ __global__ void __launch_bounds__(WM * WN * 64)
   }  // tile loop
 }
 
+// ---------------------------------------------------------------------------
+// fp8 E4M3 weights with few rows per group (decode batches): the weight
+// stream is the whole cost, so the tile keeps two 40 KB stages in flight per
+// CU and copies whole 128-byte lines.  BM = 32 token rows, BN = 256 weight
+// rows, BK = 128: one cache line of each fp8 weight row and exactly one
+// 128x128 scale block per 32-row column group per k-step.  Weights stay fp8
+// in LDS; each B fragment (8 codes) is decoded exactly to the MFMA input
+// type (every E4M3 value is representable in bf16), the k-step's
+// products accumulate unscaled, and the block scale multiplies the k-step's
+// fp32 partial sums.  Four waves, each 32 x 64 (two 32x32 MFMA columns).
+// ---------------------------------------------------------------------------
+
+// 8 E4M3 codes -> 8 bf16, exact (every E4M3 value is a bf16 value, so the
+// low 16 bits of the decoded f32 are zero).
+__device__ __forceinline__ bf16x8 decode_fp8x8(uint32_t lo, uint32_t hi) {
+  const uint32_t w[2] = {lo, hi};
+  u32x4 u;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);  // bytes 0, 1
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);   // bytes 2, 3
+    u[2 * i] = (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xffff0000u);
+    u[2 * i + 1] = (__float_as_uint(b[0]) >> 16) | (__float_as_uint(b[1]) & 0xffff0000u);
+  }
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+template <int DT, int EPI>
+struct Fp8SmallTile {
+  static_assert(DT == MOE_DTYPE_BF16, "fp8 weights pair with bf16 activations");
+  static constexpr int BM = 32, BN = 256, BK = 128, NS = 3, NW = 4;
+  static constexpr int NT = NW * 64;
+  static constexpr int TN = 2;                        // 32-column groups per wave
+  static constexpr int A_ROWB = BK * 2, B_ROWB = BK;  // 256 B (16-bit), 128 B (fp8)
+  static constexpr int A_BYTES = BM * A_ROWB, B_BYTES = BN * B_ROWB;
+  static constexpr int STAGE = A_BYTES + B_BYTES;     // 40 KB
+  static constexpr int A_BLK = A_BYTES / 1024;        // blocks of 4 A rows
+  static constexpr int B_BLK = B_BYTES / 1024;        // blocks of 8 B rows
+  static constexpr int BPW = (A_BLK + B_BLK) / NW;
+  static constexpr int JA = A_BLK / NW;
+  static constexpr int SMEM = NS * STAGE;
+  static_assert(A_BLK % NW == 0 && B_BLK % NW == 0 && 2 * BPW < 64, "blocks");
+
+  __device__ static __forceinline__ void run(const GemmArgs& p, const TileInfo& ti, int nt,
+                                             char* smem) {
+    typedef typename MfmaOp<DT>::V V;
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63;
+    const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lrow = lane & 31;
+    const int khalf = lane >> 5;
+    const int a_sub = p.a_local ? ti.base : 0;
+    const int c_sub = p.c_local ? ti.base : 0;
+    const int n0 = nt * BN;
+    const int n0h = nt * (BN / 2);
+
+    int base_row = ti.r0 - a_sub;
+    if (p.a_local && base_row > p.a_rows - 1) base_row = p.a_rows - 1;
+    const char* a_tile = uniform_ptr((const char*)p.A + (long long)base_row * p.lda * 2);
+    const char* b_tile = uniform_ptr((const char*)p.B + (long long)ti.g * p.strideB);
+    uint32_t voff[BPW];
+    int ldsoff[BPW];
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+      const int q = wn + NW * j;
+      if (j < JA) {
+        // A: 4 rows x 256 B per block; 16-byte chunk c of row r at c ^ (r & 15)
+        const int row = 4 * q + (lane >> 4);
+        const int kc = (lane & 15) ^ (row & 15);
+        int grow = ti.r0 + row;
+        grow = grow < ti.r1 ? grow : ti.r1 - 1;
+        int arow = grow - a_sub;
+        if (p.a_local && arow >= p.a_rows) arow = p.a_rows - 1;
+        voff[j] = (uint32_t)(arow - base_row) * (uint32_t)(p.lda * 2) + (uint32_t)(kc * 16);
+        ldsoff[j] = q * 1024;
+      } else {
+        // B: 8 rows x 128 B per block; 16-byte chunk c of row r at c ^ ((r >> 1) & 7)
+        const int qb = q - A_BLK;
+        const int row = 8 * qb + (lane >> 3);
+        const int kc = (lane & 7) ^ ((row >> 1) & 7);
+        int n;
+        if (EPI == EPI_SWIGLU) {
+          const int gi = row >> 5;
+          n = ((gi & 1) ? p.I : 0) + n0h + (gi >> 1) * 32 + (row & 31);
+        } else {
+          n = n0 + row;
+        }
+        voff[j] = (uint32_t)n * (uint32_t)p.ldb + (uint32_t)(kc * 16);
+        ldsoff[j] = A_BYTES + qb * 1024;
+      }
+    }
+    // scale rows of this wave's two column groups
+    const float* srow[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      int n;
+      if (EPI == EPI_SWIGLU) n = (j ? p.I : 0) + n0h + wn * 32;
+      else n = n0 + wn * 64 + j * 32;
+      srow[j] = p.Bscale + (long long)ti.g * p.strideS + (long long)(n >> 7) * (p.K >> 7);
+    }
+
+    f32x16 acc[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][v] = 0.0f;
+
+    const int nk = p.K / BK;
+    const uint32_t lds0 = lds_addr(smem);
+#define MOE_ISSUE8(st)                                                             \
+do {                                                                             \
+    const uint32_t dst_ = lds0 + ((st) % NS) * STAGE;                              \
+    const char* ak_ = a_tile + (st) * A_ROWB;                                      \
+    const char* bk_ = b_tile + (st) * B_ROWB;                                      \
+    _Pragma("unroll") for (int j = 0; j < BPW; ++j)                                \
+      dma16(j < JA ? ak_ : bk_, voff[j], dst_ + ldsoff[j]);                        \
+} while (0)
+
+    lds_barrier();  // every wave is done with the previous tile's stages
+    MOE_ISSUE8(0);
+    if (nk > 1) MOE_ISSUE8(1);
+    for (int kt = 0; kt < nk; ++kt) {
+      // stage kt landed (stage kt+1 may be in flight), visible to all waves;
+      // every wave is done reading stage kt-1, whose buffer takes kt+2
+      if (kt + 1 < nk) wait_vmcnt<BPW>(); else wait_vmcnt<0>();
+      __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x7 << 4) | ((0x3F >> 4) << 14));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (kt + 2 < nk) MOE_ISSUE8(kt + 2);
+      float sc[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sc[j] = srow[j][kt];
+      const char* As = smem + (kt % NS) * STAGE;
+      const char* Bs = As + A_BYTES;
+      f32x16 part[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) part[j][v] = 0.0f;
+#pragma unroll
+      for (int s8 = 0; s8 < BK / 16; ++s8) {
+        const V a = *(const V*)(As + lrow * A_ROWB + (((2 * s8 + khalf) ^ (lrow & 15)) << 4));
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int brow = wn * 64 + j * 32 + lrow;
+          const uint2 q8 = *(const uint2*)(Bs + brow * B_ROWB +
+                                          ((s8 ^ ((brow >> 1) & 7)) << 4) + khalf * 8);
+          part[j] = MfmaOp<DT>::run(a, decode_fp8x8(q8.x, q8.y), part[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[j][v] += sc[j] * part[j][v];
+    }
+#undef MOE_ISSUE8
+
+    const int rsub = khalf * 4;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int grow = ti.r0 + (v >> 2) * 8 + rsub + (v & 3);
+      if (grow >= ti.r1) continue;
+      const long long crow = grow - c_sub;
+      if (p.c_local && crow >= p.c_rows) continue;
+      uint16_t* C = (uint16_t*)p.C;
+      if (EPI == EPI_SWIGLU) {
+        const float h = silu_mul(acc[0][v], acc[1][v]);
+        C[crow * p.ldc + n0h + wn * 32 + lrow] = Act<DT>::store(h);
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          float y = acc[j][v];
+          if (EPI == EPI_GELU) y = gelu_erf(y);
+          C[crow * p.ldc + n0 + wn * 64 + j * 32 + lrow] = Act<DT>::store(y);
+        }
+      }
+    }
+  }
+};
+
+template <int DT, int EPI>
+__global__ void __launch_bounds__(256) grouped_gemm_fp8s(GemmArgs p) {
+  typedef Fp8SmallTile<DT, EPI> Tile;
+  __shared__ __attribute__((aligned(1024))) char smem[Tile::SMEM];
+  __shared__ int s_pre[1024];
+  __shared__ int s_scan[Tile::NT];
+  const int total_m = build_mtile_table<Tile::NT, Tile::BM>(p, s_pre, s_scan);
+  int t_first, t_end, t_stride;
+  xcd_share(total_m * p.n_tiles, t_first, t_end, t_stride);
+  for (int t = t_first; t < t_end; t += t_stride) {
+    int mt, nt;
+    const TileInfo ti = band_tile<Tile::BM>(p, s_pre, t, p.n_tiles, p.gm, mt, nt);
+    Tile::run(p, ti, nt, smem);
+  }
+}
+
 template <int DT, int EPI, int BM, int BN, int WM, int WN>
 __global__ void __launch_bounds__(WM * WN * 64)
     grouped_gemm_dma(GemmArgs p) {
@@ -436,6 +632,17 @@ int run_dma(GemmArgs a, int max_rows, int gm, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+template <int DT, int EPI>
+int run_fp8s(GemmArgs a, int max_rows, hipStream_t s) {
+  if (a.Nb % 256 || a.K % 128) return MOE_ERR_UNSUPPORTED;
+  if ((long long)a.Nb * a.ldb >= (1ll << 32)) return MOE_ERR_UNSUPPORTED;
+  if (a.offsets && a.n_groups > 1024) return MOE_ERR_UNSUPPORTED;
+  auto kern = grouped_gemm_fp8s<DT, EPI>;
+  const dim3 grid = persistent_grid(kern, 256, a, max_rows, 32, 256, 1);
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 // Relative MFMA efficiency of each tile shape (larger wave tiles need fewer
 // LDS reads per MFMA) used to pick a shape; rounds of 256 workgroups model the
 // tail of the last wave of tiles.
@@ -447,13 +654,19 @@ struct TileShape {
 template <int DT, int WK, int EPI>
 int pick_tile(GemmArgs a, int max_rows, hipStream_t s) {
   if (EPI == EPI_F32) {
+    // router logits: one n-tile of 256 experts reads each token row once
+    if (WK == W_SAME && a.Nb % 256 == 0) return run_dma<DT, EPI, 64, 256, 1, 4>(a, max_rows, 4, s);
     if (WK == W_SAME) return run_dma<DT, EPI, 64, 128, 2, 2>(a, max_rows, 4, s);
     return run_mfma<DT, WK, EPI, 64, 128, 2, 2>(a, max_rows, 4, s);
   }
   const int groups = a.offsets ? a.n_groups : 1;
   const int rows = a.offsets ? max_rows : a.dense_M;
   const double avg = (double)rows / (groups > 0 ? groups : 1);
-  if (avg <= 48.0) return run_mfma<DT, WK, EPI, 32, 256, 1, 4>(a, max_rows, 1, s);
+  if (avg <= 48.0) {
+    if constexpr (WK == W_FP8 && DT == MOE_DTYPE_BF16 && EPI != EPI_F32)
+      return run_fp8s<DT, EPI>(a, max_rows, s);
+    return run_mfma<DT, WK, EPI, 32, 256, 1, 4>(a, max_rows, 1, s);
+  }
   const TileShape shapes[2] = {{256, 256, 1.0f}, {128, 256, 0.8f}};
   int best = 0;
   double best_t = 1e300;

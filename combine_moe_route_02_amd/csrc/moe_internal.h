@@ -35,6 +35,19 @@ struct GemmArgs {
   int gm;                 // m-tiles per band in the tile order
 };
 
+// Column slices for the one-wave-per-token row kernels (gather, combine):
+// a batch of few tokens is cut into slices of whole 64-chunk groups so that
+// about 2048 waves are in flight; cps = 16-byte chunks per slice.
+inline void row_slices(int T, int nch, int& slices, int& cps) {
+  const int groups = (nch + 63) / 64;
+  int want = T > 0 ? (2048 + T - 1) / T : 1;
+  if (want > groups) want = groups;
+  if (want < 1) want = 1;
+  const int gps = (groups + want - 1) / want;  // 64-chunk groups per slice
+  cps = gps * 64;
+  slices = (nch + cps - 1) / cps;
+}
+
 // GEMM launchers; return MOE_OK / MOE_ERR_UNSUPPORTED / MOE_ERR_HIP.
 int launch_grouped_gemm(int act_dtype, int w_dtype, int epi, GemmArgs a,
                         int max_rows, hipStream_t stream);

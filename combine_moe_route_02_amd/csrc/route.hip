@@ -102,37 +102,62 @@ __device__ __forceinline__ void load8(const typename Act<DT>::T* p, float* f) {
   }
 }
 
-// Router projection for a few experts: one wave handles TPW tokens, lanes
-// stride over H in 8-element chunks, E <= EMAX accumulators per token.
-template <int DT, int TPW, int EMAX>
+// Router projection on the vector ALUs: one wave computes TPW tokens x EB
+// experts (expert block blockIdx.y); lanes stride over H in 8-element
+// chunks, two chunks per step whose loads (kept packed until use) are all
+// issued before the FMAs, so each wave keeps 2 * (TPW + EB) 16-byte loads in
+// flight.  Used when the projection is too small or too narrow for matrix
+// tiles (few experts, or a decode batch of few tokens).
+template <int DT, int TPW, int EB>
 __global__ void __launch_bounds__(256)
     router_valu_kernel(const void* __restrict__ x, const void* __restrict__ wr, int T,
                        int H, int E, float* __restrict__ logits) {
   typedef typename Act<DT>::T ST;
+  constexpr int CPE = DT == MOE_DTYPE_F32 ? 2 : 1;  // 16-byte loads per 8 elements
   const int lane = lane_id();
   const int wave = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
   const int t0 = wave * TPW;
+  const int e0 = (int)blockIdx.y * EB;
   if (t0 >= T) return;
-  float acc[TPW][EMAX];
+  float acc[TPW][EB];
 #pragma unroll
   for (int a = 0; a < TPW; ++a)
 #pragma unroll
-    for (int e = 0; e < EMAX; ++e) acc[a][e] = 0.0f;
+    for (int e = 0; e < EB; ++e) acc[a][e] = 0.0f;
   const ST* X = (const ST*)x;
   const ST* W = (const ST*)wr;
-  const int nch = H >> 3;
-  for (int c = lane; c < nch; c += 64) {
-    float xf[TPW][8];
+  const uint4* xrow[TPW];
+  const uint4* wrow[EB];
 #pragma unroll
-    for (int a = 0; a < TPW; ++a) {
-      const int t = min(t0 + a, T - 1);
-      load8<DT>(X + (long long)t * H + c * 8, xf[a]);
+  for (int a = 0; a < TPW; ++a) xrow[a] = (const uint4*)(X + (long long)min(t0 + a, T - 1) * H);
+#pragma unroll
+  for (int e = 0; e < EB; ++e) wrow[e] = (const uint4*)(W + (long long)min(e0 + e, E - 1) * H);
+  const int nch = H >> 3;
+  for (int c = lane; c < nch; c += 128) {
+    const bool two = c + 64 < nch;
+    uint4 xq[2][TPW][CPE], wq[2][EB][CPE];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int cc = (u == 0 || two) ? c + 64 * u : c;
+#pragma unroll
+      for (int a = 0; a < TPW; ++a)
+#pragma unroll
+        for (int h = 0; h < CPE; ++h) xq[u][a][h] = xrow[a][cc * CPE + h];
+#pragma unroll
+      for (int e = 0; e < EB; ++e)
+#pragma unroll
+        for (int h = 0; h < CPE; ++h) wq[u][e][h] = wrow[e][cc * CPE + h];
     }
 #pragma unroll
-    for (int e = 0; e < EMAX; ++e) {
-      if (e < E) {
+    for (int u = 0; u < 2; ++u) {
+      if (u == 1 && !two) break;
+      float xf[TPW][8];
+#pragma unroll
+      for (int a = 0; a < TPW; ++a) load8<DT>((const ST*)xq[u][a], xf[a]);
+#pragma unroll
+      for (int e = 0; e < EB; ++e) {
         float wf[8];
-        load8<DT>(W + (long long)e * H + c * 8, wf);
+        load8<DT>((const ST*)wq[u][e], wf);
 #pragma unroll
         for (int a = 0; a < TPW; ++a)
 #pragma unroll
@@ -143,11 +168,9 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
   for (int a = 0; a < TPW; ++a) {
 #pragma unroll
-    for (int e = 0; e < EMAX; ++e) {
-      if (e < E) {
-        const float v = wave_sum(acc[a][e]);
-        if (lane == 0 && t0 + a < T) logits[(long long)(t0 + a) * E + e] = v;
-      }
+    for (int e = 0; e < EB; ++e) {
+      const float v = wave_sum(acc[a][e]);
+      if (lane == 0 && t0 + a < T && e0 + e < E) logits[(long long)(t0 + a) * E + e0 + e] = v;
     }
   }
 }
@@ -158,20 +181,16 @@ template <int DT>
 int launch_router_valu(const void* x, const void* wr, int T, int H, int E,
                        float* logits, hipStream_t s) {
   const int waves_per_block = 4;
-  if (E <= 16) {
-    constexpr int TPW = 4;
-    const int waves = (T + TPW - 1) / TPW;
-    hipLaunchKernelGGL((router_valu_kernel<DT, TPW, 16>),
-                       dim3((waves + waves_per_block - 1) / waves_per_block),
-                       dim3(256), 0, s, x, wr, T, H, E, logits);
-  } else if (E <= 128) {
-    const int waves = T;
-    hipLaunchKernelGGL((router_valu_kernel<DT, 1, 128>),
-                       dim3((waves + waves_per_block - 1) / waves_per_block),
-                       dim3(256), 0, s, x, wr, T, H, E, logits);
-  } else {
-    return MOE_ERR_UNSUPPORTED;
-  }
+#define MOE_ROUTER(TPW, EB)                                                          \
+  do {                                                                               \
+    const int waves = (T + (TPW) - 1) / (TPW);                                       \
+    hipLaunchKernelGGL((router_valu_kernel<DT, TPW, EB>),                            \
+                       dim3((waves + waves_per_block - 1) / waves_per_block,        \
+                            (E + (EB) - 1) / (EB)),                                  \
+                       dim3(256), 0, s, x, wr, T, H, E, logits);                     \
+  } while (0)
+  MOE_ROUTER(4, 8);
+#undef MOE_ROUTER
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -199,8 +218,10 @@ int route_impl(const void* x, const void* w_router, int act_dtype, const float* 
   if (T == 0) return MOE_OK;
   if (w_router) {
     int st;
+    // matrix tiles for many experts and enough tokens to fill the chip;
+    // the vector kernel otherwise (few experts, or a small decode batch)
     const bool mfma = act_dtype != MOE_DTYPE_F32 && E >= 128 && E % 128 == 0 &&
-                      H % 64 == 0;
+                      H % 64 == 0 && T >= 1024;
     if (mfma) {
       GemmArgs a{};
       a.A = x;

@@ -68,7 +68,6 @@ def _route(**kw):
     (dict(H=12), L.MOE_ERR_ARG), (dict(logits=None), L.MOE_ERR_ARG),
     (dict(invt=float("nan")), L.MOE_ERR_ARG), (dict(invt=-1.0), L.MOE_ERR_ARG),
     (dict(T=1 << 28, k=8), L.MOE_ERR_ARG),
-    (dict(E=200, k=2), L.MOE_ERR_UNSUPPORTED),
 ])
 def test_route_validation(kw, code):
     assert _route(**kw) == code

@@ -36,7 +36,9 @@ GRID = [
     small("f32_gelu", 255, 128, 8, 2, 256, act_dtype=F32, act=GELU, seed_off=4),
     small("fp8_ep_share", 64, 256, 256, 8, 128, w_dtype=FP8_E4M3, gate=SIGMOID,
           e_begin=0, e_end=32, remote=True, seed_off=5),
-    small("bf16_router_mfma", 129, 256, 256, 8, 128, gate=SIGMOID, seed_off=6),
+    small("bf16_router_mfma", 1100, 256, 256, 8, 128, gate=SIGMOID, seed_off=6),
+    small("bf16_router_valu_e256", 129, 256, 256, 8, 128, gate=SIGMOID, seed_off=16),
+    small("router_valu_e200", 70, 256, 200, 4, 128, seed_off=17),
     small("dense_e1", 100, 256, 1, 1, 128, renorm=True, seed_off=7),
     small("k_equals_e", 50, 256, 4, 4, 128, seed_off=8),
     small("one_token", 1, 256, 8, 2, 128, seed_off=9),
@@ -44,6 +46,11 @@ GRID = [
     small("no_local_expert", 90, 256, 8, 2, 128, e_begin=4, e_end=4, remote=True,
           seed_off=11),
     small("f16_e64_k1", 513, 256, 64, 1, 128, act_dtype=F16, seed_off=12),
+    # fp8 weights: decode tile (few rows per expert, some experts over one
+    # 32-row tile), GELU, and the many-rows fp8 path
+    small("fp8_multi_mtile", 96, 256, 8, 2, 256, w_dtype=FP8_E4M3, seed_off=13),
+    small("fp8_gelu", 80, 256, 8, 2, 256, w_dtype=FP8_E4M3, act=GELU, seed_off=14),
+    small("fp8_large_m", 400, 256, 8, 2, 256, w_dtype=FP8_E4M3, seed_off=15),
 ]
 
 
