@@ -258,7 +258,7 @@ __global__ void __launch_bounds__(WM * WN * 64)
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           float y = acc[i][j][v];
-          if (EPI == EPI_GELU) y = gelu_erf(y);
+          if (EPI == EPI_GELU) y = gelu_erf16(y);
           C[crow * p.ldc + n0 + wn * WTN + j * 32 + lrow] = Act<DT>::store(y);
         }
       }
@@ -439,7 +439,7 @@ do {                                                                            
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           float y = acc[j][v];
-          if (EPI == EPI_GELU) y = gelu_erf(y);
+          if (EPI == EPI_GELU) y = gelu_erf16(y);
           C[crow * p.ldc + n0 + wn * 64 + j * 32 + lrow] = Act<DT>::store(y);
         }
       }
@@ -683,12 +683,12 @@ int pick_tile(GemmArgs a, int max_rows, hipStream_t s) {
       best = c;
     }
   }
-  if (WK == W_SAME) {
+  if constexpr (WK == W_SAME) {
     if (best == 0) return run_dma<DT, EPI, 256, 256, 2, 2>(a, max_rows, 8, s);
     return run_dma<DT, EPI, 128, 256, 2, 2>(a, max_rows, 8, s);
+  } else {
+    return run_mfma<DT, WK, EPI, 128, 256, 2, 2>(a, max_rows, 8, s);
   }
-  if (best == 0) return run_mfma<DT, WK, EPI, 256, 256, 2, 2>(a, max_rows, 8, s);
-  return run_mfma<DT, WK, EPI, 128, 256, 2, 2>(a, max_rows, 8, s);
 }
 
 template <int EPI>

@@ -132,12 +132,37 @@ struct MfmaOp<MOE_DTYPE_F16> {
   }
 };
 
+// One accumulator value read into a vector register at this point of the
+// program (a plain use lets the compiler copy every accumulator out at once).
+__device__ __forceinline__ float acc_read(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
+// silu(g) * u with the hardware exp2 and reciprocal (each within about one
+// ulp of float32; the result is rounded to 16 bits afterwards).
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + __expf(-g)) * u;
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 __device__ __forceinline__ float gelu_erf(float a) {
   return 0.5f * a * (1.0f + erff(a * 0.70710678118654752f));
+}
+
+// GELU for 16-bit outputs, with erf from Abramowitz & Stegun formula 7.1.26
+// (|error| <= 1.5e-7, far below 16-bit rounding): inline and short, where
+// the library erf can end up as a call that forces every live accumulator
+// register out to memory.
+__device__ __forceinline__ float gelu_erf16(float a) {
+  const float x = a * 0.70710678118654752f;
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
+  const float poly =
+      t * (0.254829592f +
+           t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  const float e = 1.0f - poly * __expf(-ax * ax);
+  return 0.5f * a * (1.0f + (x < 0.0f ? -e : e));
 }
 
 // ---------------------------------------------------------------------------
@@ -236,14 +261,14 @@ struct DmaTile {
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int A_BLK = BM / 8, B_BLK = BN / 8;  // 1 KB blocks of 8 rows
   static constexpr int BPW = (A_BLK + B_BLK) / NW;       // DMA blocks per wave
-  static constexpr int NPF = (BM + BN + 64 * NW - 1) / (64 * NW);  // prefetches per wave
+  static constexpr int NPA = (BM + 64 * NW - 1) / (64 * NW);  // A prefetches per wave
+  static constexpr int NPF = NPA + (BN + 64 * NW - 1) / (64 * NW);  // prefetches per wave
   static constexpr int PF_OFS = NS * STAGE;                         // scratch slots
   static constexpr int SMEM = NS * STAGE + NW * 256;
   static_assert(A_BLK % NW == 0 && B_BLK % NW == 0, "blocks per wave");
   static_assert(TM >= 1 && TN >= 1, "tile");
   static_assert(EPI != EPI_SWIGLU || (TN % 2) == 0, "swiglu pairs");
   static_assert(BPW + 2 * NPF < 64, "vmcnt range");
-  static_assert(BM % 64 == 0, "prefetch rows split at the A/B boundary per wave");
 
   __device__ static __forceinline__ void run(const GemmArgs& p, const TileInfo& ti, int nt,
                                              char* smem, const int32_t* a_gather) {
@@ -257,9 +282,7 @@ struct DmaTile {
     const int prow = lane >> 3, pchunk = lane & 7;  // DMA lane -> (row, chunk)
     // MFMA operand read of k16 substep s: logical chunk 2s + khalf of a row
     // whose swizzle is that of lrow (tile rows start at multiples of 32).
-    int swo[4];
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) swo[s4] = ((2 * s4 + khalf) ^ dma_swz(lrow)) << 4;
+    const int sw_row = dma_swz(lrow) ^ khalf;  // chunk 2 * s4 + khalf -> ^ sw_row
 
     const int a_sub = p.a_local ? ti.base : 0;
     const int c_sub = p.c_local ? ti.base : 0;
@@ -313,16 +336,14 @@ struct DmaTile {
       }
     }
 
-    // L2 prefetch rows: instruction i of this wave covers rows
-    // (i * NW + wave) * 64 + lane of [A rows | B rows] (past the end: the last
-    // B row again); each wave's 64 rows lie on one side of the boundary.
+    // L2 prefetch rows: prefetch i < NPA covers A rows (i * NW + wave) * 64 +
+    // lane, the others B rows likewise (past the end: the last row again).
     uint32_t pfoff[NPF];
-    bool pf_a[NPF];
 #pragma unroll
     for (int i = 0; i < NPF; ++i) {
-      const int r = (i * NW + wave) * 64 + lane;
-      pf_a[i] = (i * NW + wave) * 64 < BM;
-      if (pf_a[i]) {
+      if (i < NPA) {
+        int r = (i * NW + wave) * 64 + lane;
+        r = r < BM ? r : BM - 1;
         int grow = ti.r0 + r;
         grow = grow < ti.r1 ? grow : ti.r1 - 1;
         int arow;
@@ -334,7 +355,7 @@ struct DmaTile {
         }
         pfoff[i] = (uint32_t)(arow - base_row) * (uint32_t)(p.lda * 2);
       } else {
-        int row = r - BM;
+        int row = ((i - NPA) * NW + wave) * 64 + lane;
         row = row < BN ? row : BN - 1;
         int n;
         if (EPI == EPI_SWIGLU) {
@@ -371,9 +392,9 @@ do {                                                                            
     const char* As_ = smem + (stage) * STAGE;                                      \
     const char* Bs_ = As_ + A_BYTES;                                               \
     _Pragma("unroll") for (int i = 0; i < TM; ++i)                                 \
-      FA[i] = *(const V*)(As_ + (wm * WTM + i * 32 + lrow) * ROWB + swo[s4]);      \
+      FA[i] = *(const V*)(As_ + (wm * WTM + i * 32 + lrow) * ROWB + (((2 * (s4)) ^ sw_row) << 4)); \
     _Pragma("unroll") for (int j = 0; j < TN; ++j)                                 \
-      FB[j] = *(const V*)(Bs_ + (wn * WTN + j * 32 + lrow) * ROWB + swo[s4]);      \
+      FB[j] = *(const V*)(Bs_ + (wn * WTN + j * 32 + lrow) * ROWB + (((2 * (s4)) ^ sw_row) << 4)); \
 } while (0)
 #define MOE_MFMAS(FA, FB)                                                          \
 do {                                                                             \
@@ -403,7 +424,7 @@ do {                                                                            
 do {                                                                             \
     const uint32_t pdst_ = lds0 + PF_OFS + wave * 256;                             \
     _Pragma("unroll") for (int i = 0; i < NPF; ++i)                                \
-      prefetch4((pf_a[i] ? a_tile : b_tile) + MOE_KOFS(st), pfoff[i], pdst_);      \
+      prefetch4((i < NPA ? a_tile : b_tile) + MOE_KOFS(st), pfoff[i], pdst_);      \
 } while (0)
 // Wait until at most n_pf prefetch groups (issued after the stage's copies)
 // are in flight.
@@ -426,8 +447,8 @@ do {                                                                            
     if (nk > 2) MOE_PREFETCH(2);
     if (nk > 3) MOE_PREFETCH(3);
     // stage 0 landed; stage 1 and the prefetches may be in flight
+    const int npf0 = nk > 3 ? 2 : (nk > 2 ? 1 : 0);
     {
-      const int npf0 = (nk > 2) + (nk > 3);
       if (nk <= 1) wait_vmcnt<0>();
       else if (npf0 == 0) wait_vmcnt<BPW>();
       else if (npf0 == 1) wait_vmcnt<BPW + NPF>();
@@ -463,7 +484,7 @@ do {                                                                            
       MOE_PHASE();
       // prefetch groups issued after stage kt+1's copies: the prologue's two
       // for kt = 0, else the one issued with them (if any)
-      MOE_STAGE_READY(kt == 0 ? (nk > 2) + (nk > 3) : (kt + 3 < nk));
+      MOE_STAGE_READY(kt == 0 ? npf0 : (kt + 3 < nk));
       MOE_READ(st ^ 1, 0, xa, xb);
       MOE_PHASE();
       {
@@ -505,7 +526,7 @@ do {                                                                            
       MOE_MFMAS(xa, xb);
       MOE_PHASE();
       if (kt + 1 < nk) {
-        MOE_STAGE_READY(kt == 0 ? (nk > 2) + (nk > 3) : (kt + 3 < nk));
+        MOE_STAGE_READY(kt == 0 ? npf0 : (kt + 3 < nk));
         MOE_READ(st ^ 1, 0, xa, xb);
         MOE_PHASE();
       }
@@ -522,36 +543,53 @@ do {                                                                            
 #undef MOE_KOFS
 
     // Epilogue (32x32 f32 layout: lane l -> column l % 32, rows
-    // 8*(v/4) + 4*(l/32) + v%4).
+    // 8*(v/4) + 4*(l/32) + v%4).  One accumulator block (or SwiGLU pair) at a
+    // time; each value is read from the accumulator registers where it is
+    // used (acc_read), so the epilogue never holds more than a block of
+    // them in vector registers.  The s_nop wait states cover the last MFMAs'
+    // results before the first read.
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     const int rsub = khalf * 4;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+      int crow[16];
+      bool ok[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int grow = ti.r0 + wm * WTM + i * 32 + (v >> 2) * 8 + rsub + (v & 3);
-        if (grow >= ti.r1) continue;
-        const long long crow = grow - c_sub;
-        if (p.c_local && crow >= p.c_rows) continue;
-        if (EPI == EPI_SWIGLU) {
-          uint16_t* C = (uint16_t*)p.C;
+        crow[v] = grow - c_sub;
+        ok[v] = grow < ti.r1 && !(p.c_local && crow[v] >= p.c_rows);
+      }
+      if (EPI == EPI_SWIGLU) {
+        uint16_t* C = (uint16_t*)p.C;
 #pragma unroll
-          for (int jp = 0; jp < TN / 2; ++jp) {
-            const float h = silu_mul(acc[i][2 * jp][v], acc[i][2 * jp + 1][v]);
-            const int col = n0h + (wn * (TN / 2) + jp) * 32 + lrow;
-            C[crow * p.ldc + col] = Act<DT>::store(h);
+        for (int jp = 0; jp < TN / 2; ++jp) {
+          __builtin_amdgcn_sched_barrier(0);
+          const int col = n0h + (wn * (TN / 2) + jp) * 32 + lrow;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            if (!ok[v]) continue;
+            const float h = silu_mul(acc_read(acc[i][2 * jp][v]), acc_read(acc[i][2 * jp + 1][v]));
+            C[(long long)crow[v] * p.ldc + col] = Act<DT>::store(h);
           }
-        } else if (EPI == EPI_F32) {
-          float* C = (float*)p.C;
+        }
+      } else {
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            C[crow * p.ldc + n0 + wn * WTN + j * 32 + lrow] = acc[i][j][v];
-        } else {
-          uint16_t* C = (uint16_t*)p.C;
+        for (int j = 0; j < TN; ++j) {
+          __builtin_amdgcn_sched_barrier(0);
+          const int col = n0 + wn * WTN + j * 32 + lrow;
 #pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            float y = acc[i][j][v];
-            if (EPI == EPI_GELU) y = gelu_erf(y);
-            C[crow * p.ldc + n0 + wn * WTN + j * 32 + lrow] = Act<DT>::store(y);
+          for (int v = 0; v < 16; ++v) {
+            if (!ok[v]) continue;
+            float y = acc_read(acc[i][j][v]);
+            if (EPI == EPI_F32) {
+              ((float*)p.C)[(long long)crow[v] * p.ldc + col] = y;
+            } else {
+              if (EPI == EPI_GELU) y = gelu_erf16(y);
+              ((uint16_t*)p.C)[(long long)crow[v] * p.ldc + col] = Act<DT>::store(y);
+              // erf is long: one value at a time keeps its temporaries few
+              if (EPI == EPI_GELU) __builtin_amdgcn_sched_barrier(0);
+            }
           }
         }
       }
