@@ -96,7 +96,7 @@ def main():
     args = parse()
     if args.pmc_summary:
         return pmc_summary(*args.pmc_summary, calib_mib=args.calib_copy_mib or 1024,
-                           workload=args.config)
+                           workload=args.config, extra="--fused" if args.fused else "")
     if args.stats_summary:
         return stats_summary(*args.stats_summary, workload=args.config,
                              extra="--fused" if args.fused else "")
@@ -241,7 +241,7 @@ def main():
         kname = "grouped_gemm_dma (GEMM-1 + SwiGLU, moe_expert_ffn_up)"
     roof["kernel"] = kname
     roof["avg_launch_ms"] = round(gemm1_ms, 5)
-    roof["traffic"] = load_traffic("gemm1", cfg.name)
+    roof["traffic"] = load_traffic("fused" if args.fused else "gemm1", cfg.name)
 
     res = {
         "metric": METRIC,
@@ -289,7 +289,7 @@ def _per_kernel(rows, counter):
     return out
 
 
-def pmc_summary(fetch_csv, write_csv, out_path, calib_mib, workload):
+def pmc_summary(fetch_csv, write_csv, out_path, calib_mib, workload, extra=""):
     """HBM traffic per GEMM-1 launch from FETCH_SIZE / WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for the plain
     copy of calib_mib MiB (true bytes: calib_mib MiB read and written)."""
@@ -313,17 +313,19 @@ def pmc_summary(fetch_csv, write_csv, out_path, calib_mib, workload):
         epi = targs[2] if "grouped_gemm_mfma" in name else targs[1]  # SwiGLU epilogue = 1
         return epi == "1"
     gemm = [k for k in fetch if is_gemm1(k)]
-    lines = [f"# HBM traffic per launch of the GEMM-1 (+SwiGLU) kernel, workload {workload}",
+    what = ("the fused layer kernel (GEMM-1 + SwiGLU + GEMM-2 + combine)" if extra
+            else "the GEMM-1 (+SwiGLU) kernel")
+    lines = [f"# HBM traffic per launch of {what}, workload {workload}",
              "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two rocprofv3 --pmc runs,",
              f"# each scaled by the same counter's reading for a plain {calib_mib} MiB copy",
              f"# copy kernel: FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB "
              f"(true {true_kib:.0f} KiB each) -> scales {f_scale:.4f}, {w_scale:.4f}",
              "# commands (from /tmp, TMPDIR=/tmp, R = repository root):",
              f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d <dir_f> -o pmc -- python3 $R/bench.py "
-             f"--config {workload} --steps 3 --warmup 1 --no-cpu-baseline --calib-copy-mib {calib_mib}",
+             f"--config {workload} --steps 3 --warmup 1 --no-cpu-baseline --calib-copy-mib {calib_mib} {extra}".rstrip(),
              f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d <dir_w> -o pmc -- python3 $R/bench.py "
-             f"--config {workload} --steps 3 --warmup 1 --no-cpu-baseline --calib-copy-mib {calib_mib}",
-             f"#   python3 $R/bench.py --config {workload} --calib-copy-mib {calib_mib} "
+             f"--config {workload} --steps 3 --warmup 1 --no-cpu-baseline --calib-copy-mib {calib_mib} {extra}".rstrip(),
+             f"#   python3 $R/bench.py --config {workload} --calib-copy-mib {calib_mib} {extra} ".replace("  ", " ") +
              "--pmc-summary <dir_f>/pmc_counter_collection.csv <dir_w>/pmc_counter_collection.csv <out>"]
     rec = {}
     for k in gemm:
