@@ -39,8 +39,8 @@ _SIGS = {
     "moe_route": [P, P, I, P, I, I, I, I, I, I, F, P, P, P, P],
     "moe_dispatch": [P, I, P, I, I, I, I, I, I, P, P, P, P, P, P, SZ, P],
     "moe_expert_ffn": [P, P, I, I, I, I, I, I, I, P, P, P, P, I, P, P, P, SZ, P],
-    "moe_expert_ffn_up": [P, P, I, I, I, I, I, I, I, P, P, I, P, P],
-    "moe_expert_ffn_down": [P, I, I, I, I, I, I, P, P, I, P, P, P],
+    "moe_expert_ffn_up": [P, P, I, I, I, I, I, I, I, P, P, I, P, P, SZ, P],
+    "moe_expert_ffn_down": [P, I, I, I, I, I, I, P, P, I, P, P, P, SZ, P],
     "moe_combine": [P, P, P, I, I, I, I, P, P],
     "moe_layer_fused": [P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, SZ, P],
     "moe_workspace_bytes": [I, I, I, I, I, I],
@@ -107,28 +107,32 @@ def moe_dispatch(x, topk_idx, E, e_begin, e_end, counts, offsets, slot_of, row_t
         ptr(ws), ws.numel() * ws.element_size(), stream_handle(stream)))
 
 
+def _ws(ws):
+    return (ptr(ws), ws.numel() * ws.element_size()) if ws is not None else (None, 0)
+
+
 def moe_expert_ffn_up(x_perm, offsets, H, I, e_begin, e_end, max_rows, act, w13,
-                      w13_scale, h_ws, stream=None):
+                      w13_scale, h_ws, ws=None, stream=None):
     check("moe_expert_ffn_up", lib().moe_expert_ffn_up(
         ptr(x_perm), ptr(offsets), DTYPE_OF[x_perm.dtype], H, I, e_begin, e_end,
-        max_rows, act, ptr(w13), ptr(w13_scale), DTYPE_OF[w13.dtype], ptr(h_ws),
+        max_rows, act, ptr(w13), ptr(w13_scale), DTYPE_OF[w13.dtype], ptr(h_ws), *_ws(ws),
         stream_handle(stream)))
 
 
 def moe_expert_ffn_down(offsets, H, I, e_begin, e_end, max_rows, w2, w2_scale, h_ws,
-                        y_perm, stream=None):
+                        y_perm, ws=None, stream=None):
     check("moe_expert_ffn_down", lib().moe_expert_ffn_down(
         ptr(offsets), DTYPE_OF[y_perm.dtype], H, I, e_begin, e_end, max_rows, ptr(w2),
-        ptr(w2_scale), DTYPE_OF[w2.dtype], ptr(h_ws), ptr(y_perm),
+        ptr(w2_scale), DTYPE_OF[w2.dtype], ptr(h_ws), ptr(y_perm), *_ws(ws),
         stream_handle(stream)))
 
 
 def moe_expert_ffn(x_perm, offsets, H, I, e_begin, e_end, max_rows, act, w13,
-                   w13_scale, w2, w2_scale, h_ws, y_perm, stream=None):
+                   w13_scale, w2, w2_scale, h_ws, y_perm, ws=None, stream=None):
     check("moe_expert_ffn", lib().moe_expert_ffn(
         ptr(x_perm), ptr(offsets), DTYPE_OF[x_perm.dtype], H, I, e_begin, e_end,
         max_rows, act, ptr(w13), ptr(w13_scale), ptr(w2), ptr(w2_scale),
-        DTYPE_OF[w13.dtype], ptr(h_ws), ptr(y_perm), None, 0, stream_handle(stream)))
+        DTYPE_OF[w13.dtype], ptr(h_ws), ptr(y_perm), *_ws(ws), stream_handle(stream)))
 
 
 def moe_combine(y_perm, slot_of, topk_w, out, stream=None):

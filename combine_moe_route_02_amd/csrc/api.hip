@@ -79,7 +79,7 @@ int moe_dispatch(const void* x, int act_dtype, const int32_t* topk_idx, int T, i
 int moe_expert_ffn_up(const void* x_perm, const int32_t* offsets, int act_dtype, int H,
                       int I, int e_begin, int e_end, int max_rows, int act,
                       const void* w13, const float* w13_scale, int w_dtype, void* h_ws,
-                      hipStream_t stream) {
+                      void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!act_ok(act_dtype) || !weights_ok(act_dtype, w_dtype)) return MOE_ERR_UNSUPPORTED;
   if (act != MOE_ACT_SWIGLU && act != MOE_ACT_GELU) return MOE_ERR_ARG;
   if (H < 1 || I < 1 || e_begin < 0 || e_end < e_begin || max_rows < 0)
@@ -87,8 +87,10 @@ int moe_expert_ffn_up(const void* x_perm, const int32_t* offsets, int act_dtype,
   if (e_end == e_begin || max_rows == 0) return MOE_OK;
   if (!x_perm || !offsets || !w13 || !h_ws) return MOE_ERR_ARG;
   if (w_dtype == MOE_DTYPE_FP8_E4M3 && !w13_scale) return MOE_ERR_ARG;
+  if (ws && ws_bytes < ffn_ws_bytes()) return MOE_ERR_WORKSPACE;
   const int Nb = act == MOE_ACT_SWIGLU ? 2 * I : I;
   GemmArgs a{};
+  ffn_ws_attach(a, ws, ws_bytes);
   a.A = x_perm;
   a.lda = H;
   a.B = w13;
@@ -114,14 +116,17 @@ int moe_expert_ffn_up(const void* x_perm, const int32_t* offsets, int act_dtype,
 
 int moe_expert_ffn_down(const int32_t* offsets, int act_dtype, int H, int I, int e_begin,
                         int e_end, int max_rows, const void* w2, const float* w2_scale,
-                        int w_dtype, const void* h_ws, void* y_perm, hipStream_t stream) {
+                        int w_dtype, const void* h_ws, void* y_perm, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
   if (!act_ok(act_dtype) || !weights_ok(act_dtype, w_dtype)) return MOE_ERR_UNSUPPORTED;
   if (H < 1 || I < 1 || e_begin < 0 || e_end < e_begin || max_rows < 0)
     return MOE_ERR_ARG;
   if (e_end == e_begin || max_rows == 0) return MOE_OK;
   if (!offsets || !w2 || !h_ws || !y_perm) return MOE_ERR_ARG;
   if (w_dtype == MOE_DTYPE_FP8_E4M3 && !w2_scale) return MOE_ERR_ARG;
+  if (ws && ws_bytes < ffn_ws_bytes()) return MOE_ERR_WORKSPACE;
   GemmArgs a{};
+  ffn_ws_attach(a, ws, ws_bytes);
   a.A = h_ws;
   a.lda = I;
   a.B = w2;
@@ -148,11 +153,10 @@ int moe_expert_ffn(const void* x_perm, const int32_t* offsets, int act_dtype, in
                    const float* w13_scale, const void* w2, const float* w2_scale,
                    int w_dtype, void* h_ws, void* y_perm, void* ws, size_t ws_bytes,
                    hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (!act_ok(act_dtype) || !weights_ok(act_dtype, w_dtype)) return MOE_ERR_UNSUPPORTED;
   if (act != MOE_ACT_SWIGLU && act != MOE_ACT_GELU) return MOE_ERR_ARG;
   if (e_end > e_begin && max_rows > 0 && (!y_perm || !w2)) return MOE_ERR_ARG;
+  if (ws && ws_bytes < ffn_ws_bytes()) return MOE_ERR_WORKSPACE;
   // Shape checks of both halves happen before either launches.
   const int Nb = act == MOE_ACT_SWIGLU ? 2 * I : I;
   if (act_dtype == MOE_DTYPE_F32) {
@@ -162,10 +166,10 @@ int moe_expert_ffn(const void* x_perm, const int32_t* offsets, int act_dtype, in
     if (w_dtype == MOE_DTYPE_FP8_E4M3 && (H % 128 || I % 128)) return MOE_ERR_UNSUPPORTED;
   }
   int st = moe_expert_ffn_up(x_perm, offsets, act_dtype, H, I, e_begin, e_end, max_rows,
-                             act, w13, w13_scale, w_dtype, h_ws, stream);
+                             act, w13, w13_scale, w_dtype, h_ws, ws, ws_bytes, stream);
   if (st != MOE_OK) return st;
   return moe_expert_ffn_down(offsets, act_dtype, H, I, e_begin, e_end, max_rows, w2,
-                             w2_scale, w_dtype, h_ws, y_perm, stream);
+                             w2_scale, w_dtype, h_ws, y_perm, ws, ws_bytes, stream);
 }
 
 int moe_combine(const void* y_perm, const int32_t* slot_of, const float* topk_w,
@@ -203,7 +207,7 @@ size_t moe_workspace_bytes(int which, int T, int H, int E, int k, int I) {
   if (T < 0 || E < 1) return 0;
   switch (which) {
     case MOE_WS_DISPATCH: return dispatch_ws_bytes(T, E);
-    case MOE_WS_FFN: return 0;
+    case MOE_WS_FFN: return ffn_ws_bytes();
     case MOE_WS_FUSED: return fused_ws_bytes(T, H, E, k, I);
   }
   return 0;

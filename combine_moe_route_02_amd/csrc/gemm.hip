@@ -470,14 +470,62 @@ __global__ void __launch_bounds__(WM * WN * 64)
   __shared__ __attribute__((aligned(1024))) char smem[Tile::SMEM];
   __shared__ int s_pre[1024];
   __shared__ int s_scan[Tile::NT];
+  __shared__ int s_flag;
   const int total_m = build_mtile_table<Tile::NT, BM>(p, s_pre, s_scan);
-  int t_first, t_end, t_stride;
-  xcd_share(total_m * p.n_tiles, t_first, t_end, t_stride);
-  for (int t = t_first; t < t_end; t += t_stride) {
+  // Each XCD takes a contiguous slice of the tile order; its workgroups take
+  // whole rounds of tiles.  The last, partial round (rem tiles for per
+  // workgroups) is split over k when a workspace is given and at most half
+  // the workgroups would otherwise have a tile: S parts per tile, part s of
+  // local tile u on workgroup u * S + s of the XCD.
+  const int total = total_m * p.n_tiles;
+  const int xcd = (int)blockIdx.x & 7;
+  const int per = (int)gridDim.x >> 3;
+  const int idx = (int)blockIdx.x >> 3;
+  const int lo = (int)((long long)total * xcd / 8);
+  const int len = (int)((long long)total * (xcd + 1) / 8) - lo;
+  const int full = len / per;
+  const int rem = len - full * per;
+  for (int r = 0; r < full; ++r) {
     int mt, nt;
-    const TileInfo ti = band_tile<BM>(p, s_pre, t, p.n_tiles, p.gm, mt, nt);
+    const TileInfo ti = band_tile<BM>(p, s_pre, lo + r * per + idx, p.n_tiles, p.gm, mt, nt);
     Tile::run(p, ti, nt, smem, nullptr);
   }
+  if (rem == 0) return;
+  const int nk_all = p.K / Tile::BK;
+  int S = 1;
+  if (p.split_ws != nullptr && 2 * rem <= per) {
+    S = per / rem;
+    if (S > 8) S = 8;
+    if (S > nk_all / 4) S = nk_all / 4;  // at least 4 k-steps per part
+    if (S < 1) S = 1;
+  }
+  if (S == 1) {
+    if (idx < rem) {
+      int mt, nt;
+      const TileInfo ti = band_tile<BM>(p, s_pre, lo + full * per + idx, p.n_tiles, p.gm, mt, nt);
+      Tile::run(p, ti, nt, smem, nullptr);
+    }
+    return;
+  }
+  if (idx >= rem * S) return;
+  const int u = idx / S, part = idx % S;
+  int mt, nt;
+  const TileInfo ti = band_tile<BM>(p, s_pre, lo + full * per + u, p.n_tiles, p.gm, mt, nt);
+  KSplit ks;
+  ks.k0 = (int)((long long)part * nk_all / S);
+  ks.nk = (int)((long long)(part + 1) * nk_all / S) - ks.k0;
+  ks.parts = S;
+  ks.part = part;
+  ks.slot0 = p.split_ws + (long long)(((u * S) << 3) | xcd) * Tile::SLOT;
+  ks.slot_step = 8 * Tile::SLOT;
+  ks.counter = p.split_cnt + ((u << 3) | xcd);
+  ks.s_flag = &s_flag;
+  Tile::run(p, ti, nt, smem, nullptr, &ks);
+}
+
+__global__ void __launch_bounds__(256) zero_split_counters(int* c, int n) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < n) c[i] = 0;
 }
 
 // Plain fp32 grouped GEMM (64x64 tiles, 4x4 outputs per thread).
@@ -628,6 +676,16 @@ int run_dma(GemmArgs a, int max_rows, int gm, hipStream_t s) {
   if (a.offsets && a.n_groups > 1024) return MOE_ERR_UNSUPPORTED;
   auto kern = grouped_gemm_dma<DT, EPI, BM, BN, WM, WN>;
   const dim3 grid = persistent_grid(kern, WM * WN * 64, a, max_rows, BM, BN, gm);
+  // the k-split needs one slot per workgroup and one counter per tile slot
+  typedef DmaTile<DT, EPI, BM, BN, WM, WN> Tile;
+  // (slots are counted in units of a 256x256 tile's accumulators)
+  if (a.split_ws && ((long long)grid.x * Tile::SLOT > a.split_slots * 65536ll ||
+                     (long long)grid.x * 4 > kSplitCounterBytes))
+    a.split_ws = nullptr;
+  if (a.split_ws) {
+    hipLaunchKernelGGL(zero_split_counters, dim3((grid.x + 255) / 256), dim3(256), 0, s,
+                       a.split_cnt, (int)grid.x);
+  }
   hipLaunchKernelGGL(kern, grid, dim3(WM * WN * 64), 0, s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
@@ -676,7 +734,13 @@ int pick_tile(GemmArgs a, int max_rows, hipStream_t s) {
     // expected m-tiles: a segment's ragged tail costs half a tile on average
     const double mtiles = groups * (avg / t.BM + (a.offsets ? 0.5 : 1.0));
     const double tiles = mtiles * (a.Nb / t.BN);
-    const double rounds = ceil(tiles / 256.0);
+    const double G = device_cus();
+    double rounds = ceil(tiles / G);
+    if (WK == W_SAME && a.split_ws) {
+      // the last partial round is split over k when at most half full
+      const double full = floor(tiles / G), rem = tiles - full * G;
+      if (rem > 0 && 2 * rem <= G) rounds = full + 1.15 * rem / G;
+    }
     const double tm = rounds * (double)t.BM * t.BN / t.eff;
     if (tm < best_t) {
       best_t = tm;
@@ -737,6 +801,21 @@ int launch_grouped_gemm(int act_dtype, int w_dtype, int epi, GemmArgs a,
     return MOE_ERR_UNSUPPORTED;
   }
   return MOE_ERR_UNSUPPORTED;
+}
+
+// One 256x256 tile's accumulators per workgroup of a one-per-CU grid.
+size_t ffn_ws_bytes() {
+  return (size_t)kSplitCounterBytes + (size_t)device_cus() * 65536 * sizeof(float);
+}
+
+void ffn_ws_attach(GemmArgs& a, void* ws, size_t ws_bytes) {
+  a.split_ws = nullptr;
+  a.split_cnt = nullptr;
+  a.split_slots = 0;
+  if (ws == nullptr || ws_bytes <= (size_t)kSplitCounterBytes) return;
+  a.split_cnt = (int*)ws;
+  a.split_ws = (float*)((char*)ws + kSplitCounterBytes);
+  a.split_slots = (long long)((ws_bytes - kSplitCounterBytes) / (65536 * sizeof(float)));
 }
 
 }  // namespace moe

@@ -244,6 +244,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
+// A share of one tile's k-steps.  The workgroup computes k-steps
+// [k0, k0 + nk) (of BK each); with parts > 1 it stores its fp32 partial sums
+// in its own slot, and the last of the `parts` workgroups to arrive adds all
+// slots in part order (so the result does not depend on arrival order) and
+// runs the epilogue.  Part s's slot is slot0 + s * slot_step floats; each
+// thread owns a contiguous run of TM * TN * 16 floats in it.
+struct KSplit {
+  int k0, nk;
+  int parts, part;
+  float* slot0;
+  long long slot_step;
+  int* counter;
+  int* s_flag;  // one LDS int of the calling kernel
+};
+
 // One BM x BN output tile of a grouped GEMM with 16-bit weights (see the
 // stage layout above).  A rows come from p.A at row r - a_sub, or, with
 // a_gather, at row a_gather[r] (the fused kernel reads token rows of x
@@ -270,8 +285,12 @@ struct DmaTile {
   static_assert(EPI != EPI_SWIGLU || (TN % 2) == 0, "swiglu pairs");
   static_assert(BPW + 2 * NPF < 64, "vmcnt range");
 
+  static constexpr int NACC = TM * TN * 16;  // accumulators per thread
+  static constexpr long long SLOT = (long long)NT * NACC;  // floats per split slot
+
   __device__ static __forceinline__ void run(const GemmArgs& p, const TileInfo& ti, int nt,
-                                             char* smem, const int32_t* a_gather) {
+                                             char* smem, const int32_t* a_gather,
+                                             const KSplit* ks = nullptr) {
     typedef typename MfmaOp<DT>::V V;
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63;
@@ -376,7 +395,8 @@ struct DmaTile {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    const int nk = p.K / BK;
+    const int nk = ks ? ks->nk : p.K / BK;      // k-steps of this share
+    const int kbase = ks ? ks->k0 : 0;          // its first k-step
     const uint32_t lds0 = lds_addr(smem);
     // k-order rotation: tiles of different n-tiles start at different k so
     // that the workgroups of a band (which run in lockstep) do not all read
@@ -384,7 +404,7 @@ struct DmaTile {
     // concentrates the traffic on a few memory channels.  Tiles sharing an
     // n-tile share the rotation (and so their weight reads).
     const int skew = MOE_SKEW(nt, nk);
-#define MOE_KOFS(st) ((((st) + skew) < nk ? (st) + skew : (st) + skew - nk) * ROWB)
+#define MOE_KOFS(st) ((kbase + (((st) + skew) < nk ? (st) + skew : (st) + skew - nk)) * ROWB)
 
 // Fragments of k16 substep s4 of a stage into FA/FB.
 #define MOE_READ(stage, s4, FA, FB)                                                \
@@ -549,6 +569,52 @@ do {                                                                            
     // them in vector registers.  The s_nop wait states cover the last MFMAs'
     // results before the first read.
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    if (ks && ks->parts > 1) {
+      // Split tile: publish this part's sums; only the last part to arrive
+      // goes on, with the sum of all parts in part order.
+      float* mine = ks->slot0 + ks->part * ks->slot_step + (long long)tid * NACC;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; v += 4) {
+            f32x4 q;
+            q[0] = acc_read(acc[i][j][v]);
+            q[1] = acc_read(acc[i][j][v + 1]);
+            q[2] = acc_read(acc[i][j][v + 2]);
+            q[3] = acc_read(acc[i][j][v + 3]);
+            *(f32x4*)(mine + (i * TN + j) * 16 + v) = q;
+          }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const int old = __hip_atomic_fetch_add(ks->counter, 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        *ks->s_flag = old == ks->parts - 1;
+        if (old == ks->parts - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      }
+      __syncthreads();
+      if (!*ks->s_flag) return;
+      const float* base = ks->slot0 + (long long)tid * NACC;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; v += 4) {
+            const int off = (i * TN + j) * 16 + v;
+            f32x4 tot = *(const f32x4*)(base + off);
+            for (int s2 = 1; s2 < ks->parts; ++s2)
+              tot += *(const f32x4*)(base + s2 * ks->slot_step + off);
+            acc[i][j][v] = tot[0];
+            acc[i][j][v + 1] = tot[1];
+            acc[i][j][v + 2] = tot[2];
+            acc[i][j][v + 3] = tot[3];
+          }
+      asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+    }
     const int rsub = khalf * 4;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {

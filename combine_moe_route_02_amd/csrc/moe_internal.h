@@ -33,7 +33,18 @@ struct GemmArgs {
   int mt_slots;           // m-tile slots in the grid
   int n_tiles;
   int gm;                 // m-tiles per band in the tile order
+  // Optional k-split of the last, partial round of tiles (16-bit weights):
+  // fp32 partial-sum slots and arrival counters in the caller's workspace,
+  // or nullptr.
+  float* split_ws;
+  int* split_cnt;
+  long long split_slots;  // slots available (slot = one tile's accumulators)
 };
+
+// FFN workspace: arrival counters, then partial-sum slots of split tiles.
+constexpr long long kSplitCounterBytes = 16384;
+size_t ffn_ws_bytes();
+void ffn_ws_attach(GemmArgs& a, void* ws, size_t ws_bytes);
 
 // Column slices for the one-wave-per-token row kernels (gather, combine):
 // a batch of few tokens is cut into slices of whole 64-chunk groups so that

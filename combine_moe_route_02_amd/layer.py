@@ -45,7 +45,7 @@ class LayerSpec:
 class MoELayer:
     """Owns the per-call buffers of one layer shape on one device."""
 
-    def __init__(self, spec: LayerSpec, device="cuda"):
+    def __init__(self, spec: LayerSpec, device="cuda", ffn_split=True):
         s = self.spec = spec
         dev = torch.device(device)
         N = s.T * s.k
@@ -64,6 +64,11 @@ class MoELayer:
         nb = L.moe_workspace_bytes(L.WS_DISPATCH, s.T, s.H, s.E, s.k, s.I)
         self.ws = torch.empty((max(nb, 16),), dtype=torch.uint8, device=dev)
         self.ws_fused = None
+        # FFN workspace: lets the GEMMs split a sparse last round of tiles over K
+        self.ws_ffn = None
+        if ffn_split:
+            nf = L.moe_workspace_bytes(L.WS_FFN, s.T, s.H, s.E, s.k, s.I)
+            self.ws_ffn = torch.empty((nf,), dtype=torch.uint8, device=dev)
 
     # -- the four calls -----------------------------------------------------
     def route(self, x, w_router, bias=None, stream=None):
@@ -88,20 +93,21 @@ class MoELayer:
         s = self.spec
         e0, e1 = s.local
         L.moe_expert_ffn_up(self.x_perm, self.offsets, s.H, s.I, e0, e1, s.max_rows,
-                            ACTS[s.act], w13, w13_scale, self.h, stream=stream)
+                            ACTS[s.act], w13, w13_scale, self.h, ws=self.ws_ffn,
+                            stream=stream)
 
     def ffn_down(self, w2, w2_scale=None, stream=None):
         s = self.spec
         e0, e1 = s.local
         L.moe_expert_ffn_down(self.offsets, s.H, s.I, e0, e1, s.max_rows, w2, w2_scale,
-                              self.h, self.y_perm, stream=stream)
+                              self.h, self.y_perm, ws=self.ws_ffn, stream=stream)
 
     def ffn(self, w13, w2, w13_scale=None, w2_scale=None, stream=None):
         s = self.spec
         e0, e1 = s.local
         L.moe_expert_ffn(self.x_perm, self.offsets, s.H, s.I, e0, e1, s.max_rows,
                          ACTS[s.act], w13, w13_scale, w2, w2_scale, self.h, self.y_perm,
-                         stream=stream)
+                         ws=self.ws_ffn, stream=stream)
 
     def combine(self, stream=None):
         L.moe_combine(self.y_perm, self.slot_of, self.topk_w, self.out, stream=stream)

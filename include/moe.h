@@ -140,10 +140,19 @@ int moe_dispatch(const void* x, int act_dtype, const int32_t* topk_idx,
  *             there (outputs received from other GPUs).
  *  max_rows   host bound on offsets[e_end] - offsets[e_begin], typically
  *             T*min(k, E_loc); it sizes the grid.
+ *  ws         optional workspace of at least
+ *             moe_workspace_bytes(MOE_WS_FFN, ...) bytes, or NULL.  With it,
+ *             when the tiles of a GEMM leave the last round of workgroups at
+ *             most half busy, those tiles are split over K: each part stores
+ *             fp32 partial sums in the workspace and the last part to finish
+ *             adds them in part order (deterministic for a given GPU) before
+ *             the epilogue.  Contents need not be initialised; calls that
+ *             share a workspace must be ordered (same stream).  A non-NULL
+ *             workspace that is too small returns MOE_ERR_WORKSPACE.
  * Computation: fp32 accumulation; SwiGLU h = silu(x Wg^T) * (x Wu^T), GELU
  * h = gelu_erf(x W1^T), h rounded once to act_dtype; y = h W2^T rounded once.
  * Limits: H % 256 == 0 and I % 128 == 0 for 16-bit types; fp32 needs
- * H % 64 == 0 and I % 64 == 0; ws may be NULL (no workspace used).
+ * H % 64 == 0 and I % 64 == 0.
  */
 int moe_expert_ffn(const void* x_perm, const int32_t* offsets, int act_dtype,
                    int H, int I, int e_begin, int e_end, int max_rows, int act,
@@ -159,11 +168,12 @@ int moe_expert_ffn_up(const void* x_perm, const int32_t* offsets,
                       int act_dtype, int H, int I, int e_begin, int e_end,
                       int max_rows, int act, const void* w13,
                       const float* w13_scale, int w_dtype, void* h_ws,
-                      hipStream_t stream);
+                      void* ws, size_t ws_bytes, hipStream_t stream);
 int moe_expert_ffn_down(const int32_t* offsets, int act_dtype, int H, int I,
                         int e_begin, int e_end, int max_rows, const void* w2,
                         const float* w2_scale, int w_dtype, const void* h_ws,
-                        void* y_perm, hipStream_t stream);
+                        void* y_perm, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
 
 /*
  * moe_combine - gate-weighted un-permute reduction.
@@ -192,8 +202,8 @@ int moe_combine(const void* y_perm, const int32_t* slot_of,
  * Inputs are those of moe_dispatch/moe_expert_ffn/moe_combine after
  * moe_route and moe_dispatch have produced offsets, slot_of and row_token
  * (x_perm is not needed: GEMM-1 gathers its rows from x via row_token).
- * Results equal moe_expert_ffn followed by moe_combine: h_ws, y_perm (local
- * rows) and out are written.  ws must hold
+ * Results equal moe_expert_ffn (without workspace) followed by
+ * moe_combine, bit for bit: h_ws, y_perm (local rows) and out are written.  ws must hold
  * moe_workspace_bytes(MOE_WS_FUSED, ...) bytes; it is initialised by the
  * call.  Supported for 16-bit activations with 16-bit weights.
  */
@@ -205,7 +215,9 @@ int moe_layer_fused(const void* x, const int32_t* offsets,
                     void* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes needed by moe_dispatch (MOE_WS_DISPATCH), moe_expert_ffn
- * (MOE_WS_FFN; 0) or moe_layer_fused (MOE_WS_FUSED) for these sizes. */
+ * and its halves (MOE_WS_FFN: one 256 KB partial-sum slot per compute unit
+ * of the current device, plus counters) or moe_layer_fused (MOE_WS_FUSED)
+ * for these sizes. */
 size_t moe_workspace_bytes(int which, int T, int H, int E, int k, int I);
 
 /* Static, human-readable text for a status code. */

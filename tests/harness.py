@@ -52,12 +52,14 @@ def spec(cfg: LayerConfig):
                      e_end=cfg.e_end, inv_temperature=cfg.inv_temperature)
 
 
-def gpu_layer(cfg: LayerConfig, inp, fused=False):
-    """Run the whole layer through the C ABI on cuda:0; returns the MoELayer."""
+def gpu_layer(cfg: LayerConfig, inp, fused=False, split=True):
+    """Run the whole layer through the C ABI on cuda:0; returns the MoELayer.
+    split=False runs the expert GEMMs without a workspace (no k-split)."""
     from combine_moe_route_02_amd import MoELayer
     say(f"[gpu] layer {cfg.name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I} "
-        f"{cfg.act_dtype}/{cfg.w_dtype} local=[{cfg.e_begin},{cfg.e_end}) fused={fused}")
-    lay = MoELayer(spec(cfg), "cuda")
+        f"{cfg.act_dtype}/{cfg.w_dtype} local=[{cfg.e_begin},{cfg.e_end}) fused={fused} "
+        f"split={split}")
+    lay = MoELayer(spec(cfg), "cuda", ffn_split=split)
     if inp.get("y_remote") is not None:
         lay.y_perm.copy_(inp["y_remote"])
     if fused:

@@ -45,7 +45,10 @@ def test_workspace_sizes():
     # two int32 tables [E][ceil(T/256)]
     assert lib.moe_workspace_bytes(L.WS_DISPATCH, 16384, 7168, 256, 8, 2048) == 2 * 256 * 64 * 4
     assert lib.moe_workspace_bytes(L.WS_DISPATCH, 1, 8, 8, 1, 8) == 2 * 8 * 1 * 4
-    assert lib.moe_workspace_bytes(L.WS_FFN, 4096, 4096, 8, 1, 14336) == 0
+    # counters + one 256x256 fp32 partial-sum slot per compute unit (256 when
+    # the device cannot be queried)
+    ffn = lib.moe_workspace_bytes(L.WS_FFN, 4096, 4096, 8, 1, 14336)
+    assert ffn > 16384 and (ffn - 16384) % (256 * 256 * 4) == 0
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
@@ -111,10 +114,19 @@ def test_ffn_validation():
     assert f(FAKE, FAKE, L.DTYPE_BF16, 256, 128, 0, 8, 64, 5, FAKE, None, FAKE, None,
              L.DTYPE_BF16, FAKE, FAKE, None, 0, None) == L.MOE_ERR_ARG
     assert lib.moe_expert_ffn_up(FAKE, FAKE, L.DTYPE_BF16, 256, 128, 3, 2, 64, 0, FAKE,
-                                 None, L.DTYPE_BF16, FAKE, None) == L.MOE_ERR_ARG
+                                 None, L.DTYPE_BF16, FAKE, None, 0, None) == L.MOE_ERR_ARG
     # empty local range / no rows: nothing to do
     assert lib.moe_expert_ffn_up(FAKE, FAKE, L.DTYPE_BF16, 256, 128, 3, 3, 64, 0, FAKE,
-                                 None, L.DTYPE_BF16, FAKE, None) == L.MOE_OK
+                                 None, L.DTYPE_BF16, FAKE, None, 0, None) == L.MOE_OK
+    # a workspace, when given, must hold moe_workspace_bytes(MOE_WS_FFN)
+    need = lib.moe_workspace_bytes(L.WS_FFN, 4, 256, 8, 2, 128)
+    assert need > 16384
+    assert lib.moe_expert_ffn_up(FAKE, FAKE, L.DTYPE_BF16, 256, 128, 0, 8, 64, 0, FAKE,
+                                 None, L.DTYPE_BF16, FAKE, FAKE, need - 1,
+                                 None) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_expert_ffn_down(FAKE, L.DTYPE_BF16, 256, 128, 0, 8, 64, FAKE, None,
+                                   L.DTYPE_BF16, FAKE, FAKE, FAKE, 100,
+                                   None) == L.MOE_ERR_WORKSPACE
 
 
 def test_combine_and_fused_validation():

@@ -14,6 +14,7 @@ from gen.configs import BASE_SEED, BF16, F16, F32, FP8_E4M3, GELU, SIGMOID, SOFT
     SWIGLU, LayerConfig
 from gen.inputs import make_inputs
 from oracle import moe_oracle as O
+from oracle.torch_io import stored
 from tests.harness import TOL_F32, check_routing, full_parity, gpu_layer, np_stored, \
     rel_l2, say, spec, to_device
 
@@ -51,6 +52,8 @@ GRID = [
     small("fp8_multi_mtile", 96, 256, 8, 2, 256, w_dtype=FP8_E4M3, seed_off=13),
     small("fp8_gelu", 80, 256, 8, 2, 256, w_dtype=FP8_E4M3, act=GELU, seed_off=14),
     small("fp8_large_m", 400, 256, 8, 2, 256, w_dtype=FP8_E4M3, seed_off=15),
+    # long K: the GEMMs' sparse last round is split over K (parts of 4+ k-steps)
+    small("bf16_ksplit", 300, 2048, 8, 2, 1024, seed_off=18),
 ]
 
 
@@ -131,3 +134,19 @@ def test_repeat_runs_are_bitwise_identical():
     r1 = int(a.offsets[cfg.e_end])           # rows written by dispatch and the FFN
     assert torch.equal(a.x_perm[:r1], b.x_perm[:r1])
     assert torch.equal(a.h[:r1], b.h[:r1])
+
+
+def test_ksplit_matches_unsplit():
+    """The k-split of the last round changes only the fp32 summation order."""
+    cfg = small("ksplit_cmp", 300, 2048, 8, 2, 1024, seed_off=19)
+    inp = make_inputs(cfg, "cpu")
+    dev = to_device(inp)
+    a = gpu_layer(cfg, dev, split=True)
+    b = gpu_layer(cfg, dev, split=False)
+    r0, r1 = int(a.offsets[cfg.e_begin]), int(a.offsets[cfg.e_end])
+    ya = O.decode(stored(a.y_perm[r0:r1]), cfg.act_dtype)
+    yb = O.decode(stored(b.y_perm[r0:r1]), cfg.act_dtype)
+    e = rel_l2(ya, yb)
+    say(f"  split vs unsplit y_perm rel-L2 {e:.3e}")
+    assert e <= 1e-3
+    full_parity(cfg, inp, a)
