@@ -5,6 +5,7 @@ combine over one batch of synthetic tokens, every step through the C ABI of
 libmoe.so on one HIP stream, inputs already resident in HBM.
 
     python bench.py [--steps K] [--warmup W] [--config c2] [--gpus 1]
+                    [--fused] [--temperature T] [--min-prob P]
 
 Prints one JSON line: whole-layer tokens/s, plus the dominant kernel's
 roofline (GEMM-1, timed live with HIP events on the launch stream), the
@@ -58,7 +59,23 @@ def parse():
     ap.add_argument("--fused", action="store_true",
                     help="time the fused dispatch->GEMM->combine kernel instead of "
                          "the four separate calls")
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="softmax temperature of the gate (default: the workload's, 1.0)")
+    ap.add_argument("--min-prob", type=float, default=0.0,
+                    help="minimum-probability threshold of the gate (0: off)")
     return ap.parse_args()
+
+
+def gating_of(args):
+    """Workload overrides for the gating variants, and their label."""
+    kw, tag = {}, []
+    if args.temperature > 0:
+        kw["inv_temperature"] = 1.0 / args.temperature
+        tag.append(f"temperature {args.temperature:g}")
+    if args.min_prob > 0:
+        kw["min_prob"] = args.min_prob
+        tag.append(f"threshold {args.min_prob:g}")
+    return kw, (" [gate " + ", ".join(tag) + "]") if tag else ""
 
 
 def source_hash() -> str:
@@ -113,7 +130,8 @@ def main():
     from combine_moe_route_02_amd._lib import lib
 
     lib()  # fail loudly if the HIP library is missing
-    cfg = CONFIGS[args.config]
+    gate_kw, gate_tag = gating_of(args)
+    cfg = CONFIGS[args.config].with_(**gate_kw)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating {cfg.name} inputs on {dev}", file=sys.stderr, flush=True)
@@ -121,7 +139,8 @@ def main():
     tdt = inp["x"].dtype
     spec = LayerSpec(T=cfg.T, H=cfg.H, E=cfg.E, k=cfg.k, I=cfg.I, act_dtype=tdt,
                      gate=cfg.gate, renorm=cfg.renorm, act=cfg.act, e_begin=cfg.e_begin,
-                     e_end=cfg.e_end, inv_temperature=cfg.inv_temperature)
+                     e_end=cfg.e_end, inv_temperature=cfg.inv_temperature,
+                     min_prob=cfg.min_prob)
     lay = MoELayer(spec, dev)
     if inp["y_remote"] is not None:
         lay.y_perm.copy_(inp["y_remote"])
@@ -209,7 +228,8 @@ def main():
     tok_needed = int(loc_pick.any(axis=1).sum())
     disp_bytes = (tok_needed * H * ab + rows_loc * H * ab          # gather
                   + T * k * 4 * 3 + E * 4 * 2)                    # idx in, slot/row out
-    comb_bytes = T * k * H * ab + T * H * ab + T * k * 8          # rows in, out, slot+w
+    n_kept = int((idx >= 0).sum())                                # picks with a row
+    comb_bytes = n_kept * H * ab + T * H * ab + T * k * 8         # rows in, out, slot+w
     dc_gbps = (disp_bytes + comb_bytes) / ((stage_ms["dispatch"] + stage_ms["combine"]) * 1e6)
     touched = int((counts[e0:e1] > 0).sum())
     if cfg.w_dtype == "e4m3":
@@ -241,7 +261,9 @@ def main():
         kname = "grouped_gemm_dma (GEMM-1 + SwiGLU, moe_expert_ffn_up)"
     roof["kernel"] = kname
     roof["avg_launch_ms"] = round(gemm1_ms, 5)
-    roof["traffic"] = load_traffic("fused" if args.fused else "gemm1", cfg.name)
+    # counters were taken on the workload's own gating only
+    roof["traffic"] = None if gate_tag else load_traffic("fused" if args.fused else "gemm1",
+                                                         cfg.name)
 
     res = {
         "metric": METRIC,
@@ -257,9 +279,9 @@ def main():
         "dtype": DT_NAME[cfg.act_dtype] + ("+e4m3w" if cfg.w_dtype == "e4m3" else ""),
         "data": "synthetic (seeded generator; random-init weights)",
         "config": {"workload": f"{cfg.name}: {WORKLOAD[cfg.name]}"
-                   + (" [fused kernel]" if args.fused else ""), "tokens": T,
+                   + (" [fused kernel]" if args.fused else "") + gate_tag, "tokens": T,
                    "hidden": H, "experts": E, "local_experts": e1 - e0, "top_k": k,
-                   "ffn_inner": I, "local_rows": rows_loc},
+                   "ffn_inner": I, "local_rows": rows_loc, "kept_picks": n_kept},
         "roofline": roof,
         "stages_ms": {n: round(v, 5) for n, v in stage_ms.items()},
         "dispatch_combine_GBps": round(dc_gbps, 1),
@@ -383,7 +405,7 @@ def cpu_baseline(cfg, inp, sample_tokens: int):
     p = O.LayerParams(T=S, H=sub.H, E=sub.E, k=sub.k, I=sub.I, act_dtype=sub.act_dtype,
                       w_dtype=sub.w_dtype, gate=sub.gate, renorm=sub.renorm, act=sub.act,
                       e_begin=sub.e_begin, e_end=sub.e_end,
-                      inv_temperature=sub.inv_temperature)
+                      inv_temperature=sub.inv_temperature, min_prob=sub.min_prob)
     yr = st["y_remote"][: S * cfg.k] if st["y_remote"] is not None else None
     t0 = time.perf_counter()
     O.layer_forward(p, st["x"][:S], st["w_router"], st["bias"], st["w13"], st["w2"],

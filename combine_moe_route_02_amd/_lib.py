@@ -36,7 +36,7 @@ _lib = None
 
 P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
-    "moe_route": [P, P, I, P, I, I, I, I, I, I, F, P, P, P, P],
+    "moe_route": [P, P, I, P, I, I, I, I, I, I, F, F, P, P, P, P],
     "moe_dispatch": [P, I, P, I, I, I, I, I, I, P, P, P, P, P, P, SZ, P],
     "moe_expert_ffn": [P, P, I, I, I, I, I, I, I, P, P, P, P, I, P, P, P, SZ, P],
     "moe_expert_ffn_up": [P, P, I, I, I, I, I, I, I, P, P, I, P, P, SZ, P],
@@ -87,14 +87,14 @@ DTYPE_OF = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16,
 
 
 def moe_route(x, w_router, bias, k, gate, renorm, inv_temperature, logits, topk_idx,
-              topk_w, act_dtype=None, stream=None):
+              topk_w, act_dtype=None, stream=None, min_prob=0.0):
     T, E = logits.shape
     H = x.shape[1] if x is not None else 0
     dt = act_dtype if act_dtype is not None else DTYPE_OF[x.dtype]
     check("moe_route", lib().moe_route(
         ptr(x), ptr(w_router), dt, ptr(bias), T, H, E, k, gate, int(renorm),
-        float(inv_temperature), ptr(logits), ptr(topk_idx), ptr(topk_w),
-        stream_handle(stream)))
+        float(inv_temperature), float(min_prob), ptr(logits), ptr(topk_idx),
+        ptr(topk_w), stream_handle(stream)))
 
 
 def moe_dispatch(x, topk_idx, E, e_begin, e_end, counts, offsets, slot_of, row_token,

@@ -7,7 +7,8 @@
 namespace moe {
 int route_impl(const void* x, const void* w_router, int act_dtype, const float* bias,
                int T, int H, int E, int k, int gate, int renorm, float inv_temp,
-               float* logits, int32_t* topk_idx, float* topk_w, hipStream_t s);
+               float min_prob, float* logits, int32_t* topk_idx, float* topk_w,
+               hipStream_t s);
 int dispatch_impl(const void* x, int act_dtype, const int32_t* idx, int T, int H,
                   int E, int k, int e_begin, int e_end, int32_t* counts,
                   int32_t* offsets, int32_t* slot_of, int32_t* row_token,
@@ -45,17 +46,19 @@ extern "C" {
 
 int moe_route(const void* x, const void* w_router, int act_dtype, const float* bias,
               int T, int H, int E, int k, int gate, int renorm, float inv_temperature,
-              float* logits, int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+              float min_prob, float* logits, int32_t* topk_idx, float* topk_w,
+              hipStream_t stream) {
   if (!act_ok(act_dtype)) return MOE_ERR_UNSUPPORTED;
   if (T < 0 || E < 1 || E > 1024 || k < 1 || k > E || k > 32) return MOE_ERR_ARG;
   if (!pairs_fit(T, k) || !pairs_fit(T, E)) return MOE_ERR_ARG;
   if (gate != MOE_GATE_SOFTMAX && gate != MOE_GATE_SIGMOID) return MOE_ERR_ARG;
   if (!(inv_temperature >= 0.0f) || inv_temperature > 3.0e38f) return MOE_ERR_ARG;
+  if (!(min_prob >= 0.0f && min_prob <= 1.0f)) return MOE_ERR_ARG;
   if (T == 0) return MOE_OK;
   if (!logits || !topk_idx || !topk_w) return MOE_ERR_ARG;
   if (w_router && (!x || H < 1 || H % 8)) return MOE_ERR_ARG;
   return route_impl(x, w_router, act_dtype, bias, T, H, E, k, gate, renorm,
-                    inv_temperature, logits, topk_idx, topk_w, stream);
+                    inv_temperature, min_prob, logits, topk_idx, topk_w, stream);
 }
 
 int moe_dispatch(const void* x, int act_dtype, const int32_t* topk_idx, int T, int H,

@@ -11,7 +11,8 @@
 // weights are wave-uniform (scalar loads); each lane owns 16-byte chunks of
 // the slice, accumulates the k products in float32 in pick order and rounds
 // once.  The k loads of a chunk are independent, so each lane keeps k x 16
-// bytes in flight.
+// bytes in flight.  Picks with slot -1 (dropped by the gate threshold) add
+// nothing; a token with no kept pick gets a zero row.
 
 #include "moe_internal.h"
 
@@ -38,6 +39,10 @@ __global__ void __launch_bounds__(256)
       w[j] = topk_w[(long long)t * k + j];
     }
   }
+  // slot -1: a pick dropped by the gate threshold, nothing to add
+  bool has[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) has[j] = j < k && rows[j] >= 0;
   uint4* dst = out + (long long)t * nch;
   const int c0 = (int)blockIdx.y * cps;
   const int c1 = min(nch, c0 + cps);
@@ -45,13 +50,13 @@ __global__ void __launch_bounds__(256)
     uint4 q[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
-      if (j < k) q[j] = y_perm[rows[j] + c];
+      if (has[j]) q[j] = y_perm[rows[j] + c];
     float acc[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] = 0.0f;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-      if (j < k) {
+      if (has[j]) {
         float v[EPC];
         if (DT == MOE_DTYPE_F32) {
           v[0] = __uint_as_float(q[j].x);

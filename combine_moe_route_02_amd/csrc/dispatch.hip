@@ -23,6 +23,8 @@
 //   gather  one wave per token (and column slice, for small batches): each
 //           16-byte chunk of x[t] is loaded once and stored to every local
 //           row of that token
+// A pick of -1 (dropped by the gate threshold) is not counted, gets slot -1
+// and no row; offsets[E] is then the number of kept picks.
 
 #include "moe_internal.h"
 
@@ -40,7 +42,10 @@ __global__ void __launch_bounds__(TILE)
   const int t = tile * TILE + (int)threadIdx.x;
   if (t < T) {
     const int32_t* p = idx + (long long)t * k;
-    for (int j = 0; j < k; ++j) atomicAdd(&hist[p[j]], 1);
+    for (int j = 0; j < k; ++j) {
+      const int e = p[j];
+      if (e >= 0) atomicAdd(&hist[e], 1);  // -1: dropped by the gate threshold
+    }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += TILE)
@@ -115,7 +120,7 @@ __global__ void __launch_bounds__(TILE)
   if (valid)
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
-      if (j < k) atomicOr((unsigned long long*)&lanes_of[wave * E + pk[j]], bit);
+      if (j < k && pk[j] >= 0) atomicOr((unsigned long long*)&lanes_of[wave * E + pk[j]], bit);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += TILE) {
     int run = 0;
@@ -132,6 +137,10 @@ __global__ void __launch_bounds__(TILE)
   for (int j = 0; j < KMAX; ++j) {
     if (j >= k) break;
     const int e = pk[j];
+    if (e < 0) {  // dropped pick: no row
+      slot_of[(long long)t * k + j] = -1;
+      continue;
+    }
     const int r = offsets[e] + tile_base[(long long)e * n_tiles + tile] + wbase[wave * E + e] +
                   __popcll(lanes_of[wave * E + e] & lt);
     slot_of[(long long)t * k + j] = r;
@@ -163,7 +172,7 @@ __global__ void __launch_bounds__(TILE)
   if (valid)
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
-      if (j < k) atomicOr((unsigned long long*)&lanes_of[wave * E + pk[j]], bit);
+      if (j < k && pk[j] >= 0) atomicOr((unsigned long long*)&lanes_of[wave * E + pk[j]], bit);
   __syncthreads();
   // thread i owns experts [i * per, (i + 1) * per): prefix over the 4 waves
   // and the expert's count
@@ -210,6 +219,10 @@ __global__ void __launch_bounds__(TILE)
   for (int j = 0; j < KMAX; ++j) {
     if (j >= k) break;
     const int e = pk[j];
+    if (e < 0) {  // dropped pick: no row
+      slot_of[(long long)t * k + j] = -1;
+      continue;
+    }
     const int r = s_off[e] + wbase[wave * E + e] + __popcll(lanes_of[wave * E + e] & lt);
     slot_of[(long long)t * k + j] = r;
     row_token[r] = t;

@@ -200,13 +200,13 @@ __global__ void __launch_bounds__(WM * WN * 64) fused_layer_kernel(FusedArgs f) 
           uint4 qv[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j)
-            if (j < f.k) qv[j] = f.y_perm[rj[j] + c];
+            if (j < f.k && rj[j] >= 0) qv[j] = f.y_perm[rj[j] + c];
           float acc[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            if (j < f.k) {
+            if (j < f.k && rj[j] >= 0) {
               float v[8];
               unpack8<DT>(qv[j], v);
 #pragma unroll
@@ -224,6 +224,7 @@ __global__ void __launch_bounds__(WM * WN * 64) fused_layer_kernel(FusedArgs f) 
         for (int j = 0; j < f.k; ++j) {
           const int rjj = __shfl(row, j, 64);
           const float wjj = __shfl(w, j, 64);
+          if (rjj < 0) continue;  // dropped pick
           float v[8];
           unpack8<DT>(f.y_perm[(long long)rjj * f.nch + c], v);
 #pragma unroll

@@ -5,7 +5,10 @@
 // Gate weights are either the softmax over all experts, evaluated at the
 // picks, with an optional temperature (GPT-4 MoE page, section 4.1 step 2;
 // xDeepServe diary, section 5.3), or a sigmoid of each picked score, and
-// may be renormalised to sum 1.
+// may be renormalised to sum 1.  A minimum-probability threshold (GPT-4 MoE
+// page, section 2.3 stage 2 and its section 4.1 sketch) drops every pick
+// whose gate value is not above it: index -1, weight 0.  Gate values fall
+// with the selection order, so dropped picks are the last of a token's k.
 //
 // Selection key.  s = logit + bias (one float32 add), -0.0 made +0.0, mapped
 // to an order-preserving uint32 and placed above the complement of the
@@ -35,7 +38,8 @@ template <int EPL>
 __global__ void __launch_bounds__(256)
     topk_gate_kernel(const float* __restrict__ logits, const float* __restrict__ bias,
                      int T, int E, int k, int gate, int renorm, float inv_temp,
-                     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+                     float min_prob, int32_t* __restrict__ topk_idx,
+                     float* __restrict__ topk_w) {
   const int lane = lane_id();
   const int t = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
   if (t >= T) return;
@@ -80,12 +84,15 @@ __global__ void __launch_bounds__(256)
   } else {
     w = 1.0f / (1.0f + expf(-sj));
   }
+  // threshold on the gate value before renormalisation (min_prob 0: off)
+  const bool keep = !(min_prob > 0.0f) || w > min_prob;
+  if (!keep) w = 0.0f;
   if (renorm) {
     const float tot = wave_sum(lane < k ? w : 0.0f);
-    w = w / tot;
+    w = tot > 0.0f ? w / tot : 0.0f;
   }
   if (lane < k) {
-    topk_idx[(long long)t * k + lane] = (int32_t)(~(uint32_t)mine);
+    topk_idx[(long long)t * k + lane] = keep ? (int32_t)(~(uint32_t)mine) : -1;
     topk_w[(long long)t * k + lane] = w;
   }
 }
@@ -195,12 +202,12 @@ int launch_router_valu(const void* x, const void* wr, int T, int H, int E,
 }
 
 int launch_topk(const float* logits, const float* bias, int T, int E, int k,
-                int gate, int renorm, float inv_temp, int32_t* idx, float* w,
-                hipStream_t s) {
+                int gate, int renorm, float inv_temp, float min_prob, int32_t* idx,
+                float* w, hipStream_t s) {
   const dim3 grid((T + 3) / 4), block(256);
 #define MOE_TOPK(EPL)                                                         \
   hipLaunchKernelGGL((topk_gate_kernel<EPL>), grid, block, 0, s, logits, bias, \
-                     T, E, k, gate, renorm, inv_temp, idx, w)
+                     T, E, k, gate, renorm, inv_temp, min_prob, idx, w)
   if (E <= 64) MOE_TOPK(1);
   else if (E <= 128) MOE_TOPK(2);
   else if (E <= 256) MOE_TOPK(4);
@@ -214,7 +221,8 @@ int launch_topk(const float* logits, const float* bias, int T, int E, int k,
 
 int route_impl(const void* x, const void* w_router, int act_dtype, const float* bias,
                int T, int H, int E, int k, int gate, int renorm, float inv_temp,
-               float* logits, int32_t* topk_idx, float* topk_w, hipStream_t s) {
+               float min_prob, float* logits, int32_t* topk_idx, float* topk_w,
+               hipStream_t s) {
   if (T == 0) return MOE_OK;
   if (w_router) {
     int st;
@@ -247,7 +255,8 @@ int route_impl(const void* x, const void* w_router, int act_dtype, const float* 
     }
     if (st != MOE_OK) return st;
   }
-  return launch_topk(logits, bias, T, E, k, gate, renorm, inv_temp, topk_idx, topk_w, s);
+  return launch_topk(logits, bias, T, E, k, gate, renorm, inv_temp, min_prob, topk_idx,
+                     topk_w, s);
 }
 
 }  // namespace moe

@@ -31,6 +31,7 @@ class LayerSpec:
     e_begin: int = 0
     e_end: int = -1          # -1: all experts are local
     inv_temperature: float = 1.0
+    min_prob: float = 0.0    # gate threshold; 0 = off
 
     @property
     def local(self):
@@ -74,14 +75,15 @@ class MoELayer:
     def route(self, x, w_router, bias=None, stream=None):
         s = self.spec
         L.moe_route(x, w_router, bias, s.k, GATES[s.gate], s.renorm, s.inv_temperature,
-                    self.logits, self.topk_idx, self.topk_w, stream=stream)
+                    self.logits, self.topk_idx, self.topk_w, stream=stream,
+                    min_prob=s.min_prob)
 
     def route_from_logits(self, bias=None, stream=None):
         """Top-k gating on the scores already in self.logits."""
         s = self.spec
         L.moe_route(None, None, bias, s.k, GATES[s.gate], s.renorm, s.inv_temperature,
                     self.logits, self.topk_idx, self.topk_w,
-                    act_dtype=L.DTYPE_OF[s.act_dtype], stream=stream)
+                    act_dtype=L.DTYPE_OF[s.act_dtype], stream=stream, min_prob=s.min_prob)
 
     def dispatch(self, x, stream=None):
         s = self.spec

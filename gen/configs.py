@@ -50,6 +50,7 @@ class LayerConfig:
     expert_std: Optional[float] = None   # None -> N(0,1)/sqrt(fan_in)
     remote_rows: bool = False      # pre-filled "received" rows for non-local experts
     inv_temperature: float = 1.0
+    min_prob: float = 0.0          # gate threshold (0: off)
 
     @property
     def E_loc(self) -> int:

@@ -75,16 +75,25 @@ enum moe_ws_kind { MOE_WS_DISPATCH = 0, MOE_WS_FFN = 1, MOE_WS_FUSED = 2 };
  *  gate      MOE_GATE_SOFTMAX: w = softmax over all E of (s * inv_temperature)
  *            evaluated at the picks; MOE_GATE_SIGMOID: w = 1/(1+exp(-s)).
  *            s = logits + bias (one float32 addition).
- *  renorm    nonzero: the k weights of a token are divided by their sum.
+ *  renorm    nonzero: the kept weights of a token are divided by their sum
+ *            (a token with no kept pick keeps zero weights).
+ *  min_prob  minimum-probability threshold in [0, 1] (GPT-4 MoE page,
+ *            section 2.3 stage 2 and its section 4.1 sketch).  When it is
+ *            above 0, a pick whose gate value (before renorm) is not above
+ *            min_prob is dropped: topk_idx -1 and topk_w 0.  Gate values fall
+ *            with the pick order, so dropped picks are the last ones of a
+ *            token.  0 turns the threshold off.
  *  logits    [T][E] float32 (output, or input when w_router is NULL).
  *  topk_idx  [T][k] int32 output: experts by descending s, ties to the lower
- *            index (-0.0 ties with +0.0).
+ *            index (-0.0 ties with +0.0); -1 for a dropped pick.
  *  topk_w    [T][k] float32 output: gate weights in the same order.
- * Limits: 1 <= k <= E <= 1024, k <= 32, H % 8 == 0.
+ * Limits: 1 <= k <= E <= 1024, k <= 32, H % 8 == 0.  An inv_temperature
+ * that is negative or not finite, or a min_prob outside [0, 1] (or NaN),
+ * returns MOE_ERR_ARG.
  */
 int moe_route(const void* x, const void* w_router, int act_dtype,
               const float* bias, int T, int H, int E, int k, int gate,
-              int renorm, float inv_temperature, float* logits,
+              int renorm, float inv_temperature, float min_prob, float* logits,
               int32_t* topk_idx, float* topk_w, hipStream_t stream);
 
 /*
@@ -98,12 +107,16 @@ int moe_route(const void* x, const void* w_router, int act_dtype,
  * 5.2).
  *
  *  x          [T][H] act_dtype.
- *  topk_idx   [T][k] int32, each in [0, E), distinct within a token.
- *  counts     [E]   int32 output: (token, pick) pairs per expert.
- *  offsets    [E+1] int32 output: exclusive prefix sum, offsets[E] = T*k.
+ *  topk_idx   [T][k] int32, each in [0, E) and distinct within a token, or
+ *             -1 for a pick dropped by moe_route's threshold.
+ *  counts     [E]   int32 output: kept (token, pick) pairs per expert.
+ *  offsets    [E+1] int32 output: exclusive prefix sum; offsets[E] is the
+ *             number of kept picks (T*k without a threshold).
  *  slot_of    [T][k] int32 output: layout row of pick j of token t
- *             = offsets[e] + (number of earlier tokens that picked e).
- *  row_token  [T*k] int32 output: inverse of slot_of (token of each row).
+ *             = offsets[e] + (number of earlier tokens that picked e);
+ *             -1 for a dropped pick.
+ *  row_token  [T*k] int32 output: inverse of slot_of (token of each row);
+ *             entries at and past offsets[E] are not written.
  *  x_perm     [T*k][H] act_dtype output: x_perm[r] = x[row_token[r]] for the
  *             rows of local experts e_begin <= e < e_end only (global row
  *             numbering; other rows are not written).
@@ -185,7 +198,9 @@ int moe_expert_ffn_down(const int32_t* offsets, int act_dtype, int H, int I,
  *  y_perm  [T*k][H] act_dtype (global row numbering).
  *  slot_of [T][k] int32, topk_w [T][k] float32 (from dispatch / route).
  *  out     [T][H] act_dtype: out[t] = sum_j topk_w[t][j] * y_perm[slot_of[t][j]],
- *          accumulated in float32 in pick order and rounded once.
+ *          accumulated in float32 in pick order and rounded once.  Picks
+ *          with slot_of -1 (dropped by moe_route's threshold) add nothing;
+ *          a token with no kept pick gets a zero row.
  */
 int moe_combine(const void* y_perm, const int32_t* slot_of,
                 const float* topk_w, int act_dtype, int T, int H, int k,
@@ -203,7 +218,8 @@ int moe_combine(const void* y_perm, const int32_t* slot_of,
  * moe_route and moe_dispatch have produced offsets, slot_of and row_token
  * (x_perm is not needed: GEMM-1 gathers its rows from x via row_token).
  * Results equal moe_expert_ffn (without workspace) followed by
- * moe_combine, bit for bit: h_ws, y_perm (local rows) and out are written.  ws must hold
+ * moe_combine, bit for bit: h_ws, y_perm (local rows) and out are written
+ * (dropped picks, slot_of -1, as in moe_combine).  ws must hold
  * moe_workspace_bytes(MOE_WS_FUSED, ...) bytes; it is initialised by the
  * call.  Supported for 16-bit activations with 16-bit weights.
  */

@@ -18,7 +18,10 @@ What it computes, step by step, with the passage each step follows:
    optionally renormalised to sum 1 (GPT-4 MoE page, section 4.1 step 2
    sketch: softmax over all experts, then top-k, weights = the selected
    probabilities; section 2.3 and the xDeepServe diary section 5.3 for the
-   temperature, default 1.0).
+   temperature, default 1.0).  With a minimum-probability threshold (GPT-4
+   MoE page, section 2.3 stage 2, and the same sketch's mask) a pick whose
+   gate value is not above it is dropped: index -1, weight 0, no layout row,
+   nothing to combine.
 3. Dispatch: per-expert counts, their exclusive prefix sum, and a dense
    expert-contiguous layout in which each token is written once per chosen
    expert (DySHARP page, section 1: dispatch sends one token to its k
@@ -205,36 +208,65 @@ def topk_select(s: np.ndarray, k: int) -> np.ndarray:
     return order[:, :k].astype(np.int32)
 
 
-def gate_weights(s: np.ndarray, idx: np.ndarray, gate: str, renorm: bool,
-                 inv_temperature: float = 1.0) -> np.ndarray:
-    """Gate weight of each pick, computed in float64 and stored as float32.
+def raw_gate(s: np.ndarray, idx: np.ndarray, gate: str,
+             inv_temperature: float = 1.0) -> np.ndarray:
+    """Gate value of each pick before any threshold or renormalisation, float64.
 
     softmax: p_e = exp((s_e - max s) * inv_tau) / sum_e' exp((s_e' - max s) * inv_tau)
-             over all experts, w_j = p at the j-th pick;
-    sigmoid: w_j = 1 / (1 + exp(-s at the j-th pick));
-    renorm:  w_j /= sum_j w_j.
+             over all experts, evaluated at the j-th pick;
+    sigmoid: 1 / (1 + exp(-s at the j-th pick)).
+    Entries of ``idx`` equal to -1 give 0.
     """
     s64 = s.astype(np.float64)
+    ii = np.maximum(idx.astype(np.int64), 0)
     if gate == "softmax":
         z = (s64 - s64.max(axis=1, keepdims=True)) * float(inv_temperature)
         p = np.exp(z)
         p = p / p.sum(axis=1, keepdims=True)
-        w = np.take_along_axis(p, idx.astype(np.int64), axis=1)
+        w = np.take_along_axis(p, ii, axis=1)
     elif gate == "sigmoid":
-        picked = np.take_along_axis(s64, idx.astype(np.int64), axis=1)
-        w = 1.0 / (1.0 + np.exp(-picked))
+        w = 1.0 / (1.0 + np.exp(-np.take_along_axis(s64, ii, axis=1)))
     else:
         raise ValueError(gate)
+    return np.where(idx >= 0, w, 0.0)
+
+
+def gate_weights(s: np.ndarray, idx: np.ndarray, gate: str, renorm: bool,
+                 inv_temperature: float = 1.0) -> np.ndarray:
+    """Gate weight of each pick, computed in float64 and stored as float32:
+    the raw gate value, then, with renorm, w_j /= sum_j w_j over the picks
+    that have an expert (a token whose picks were all dropped keeps zeros)."""
+    w = raw_gate(s, idx, gate, inv_temperature)
     if renorm:
-        w = w / w.sum(axis=1, keepdims=True)
+        tot = w.sum(axis=1, keepdims=True)
+        w = np.where(tot > 0, w / np.where(tot > 0, tot, 1.0), 0.0)
     return round_rne(w, F32).astype(np.float32)
 
 
+def threshold_mask(s: np.ndarray, idx: np.ndarray, gate: str,
+                   inv_temperature: float, min_prob: float) -> np.ndarray:
+    """True where a pick survives the minimum-probability threshold: its raw
+    gate value (float64, before renormalisation) is above min_prob (GPT-4
+    MoE page, section 2.3 stage 2 and the section 4.1 sketch: picks whose
+    probability is not above the minimum activation threshold are dropped).
+    All True when min_prob is 0: the threshold is off."""
+    if not min_prob > 0:
+        return np.ones(idx.shape, dtype=bool)
+    return raw_gate(s, idx, gate, inv_temperature) > float(min_prob)
+
+
 def route(logits: np.ndarray, bias: Optional[np.ndarray], k: int, gate: str,
-          renorm: bool, inv_temperature: float = 1.0):
-    """(topk_idx int32 [T,k], topk_w float32 [T,k]) from float32 logits."""
+          renorm: bool, inv_temperature: float = 1.0, min_prob: float = 0.0):
+    """(topk_idx int32 [T,k], topk_w float32 [T,k]) from float32 logits.
+
+    Picks dropped by the threshold have index -1 and weight 0.  Gate values
+    fall with the selection order, so the dropped picks of a token are the
+    last ones.
+    """
     s = selection_scores(logits, bias)
     idx = topk_select(s, k)
+    keep = threshold_mask(s, idx, gate, inv_temperature, min_prob)
+    idx = np.where(keep, idx, -1).astype(np.int32)
     w = gate_weights(s, idx, gate, renorm, inv_temperature)
     return idx, w
 
@@ -248,7 +280,8 @@ def expert_counts(idx: np.ndarray, E: int) -> np.ndarray:
     """counts[e] = number of (token, pick) pairs routed to expert e."""
     counts = np.zeros(E, dtype=np.int64)
     for e in idx.reshape(-1):
-        counts[e] += 1
+        if e >= 0:          # -1: a pick dropped by the gate threshold
+            counts[e] += 1
     return counts.astype(np.int32)
 
 
@@ -265,16 +298,19 @@ def layout_map(idx: np.ndarray, offsets: np.ndarray):
 
     Each expert's segment is filled in ascending token order: the j-th pick
     of token t, expert e, lands at offsets[e] + (number of earlier tokens
-    that also picked e).
+    that also picked e).  Dropped picks (index -1) get slot -1 and no row;
+    row_token entries past offsets[E] are -1.
     """
     T, k = idx.shape
     E = len(offsets) - 1
     fill = [0] * E
-    slot_of = np.empty((T, k), dtype=np.int32)
-    row_token = np.empty(T * k, dtype=np.int32)
+    slot_of = np.full((T, k), -1, dtype=np.int32)
+    row_token = np.full(T * k, -1, dtype=np.int32)
     for t in range(T):
         for j in range(k):
             e = int(idx[t, j])
+            if e < 0:
+                continue
             r = int(offsets[e]) + fill[e]
             fill[e] += 1
             slot_of[t, j] = r
@@ -338,7 +374,8 @@ def expert_ffn(X: np.ndarray, w13: np.ndarray, w2: np.ndarray, act: str,
 
 def combine(y_perm: np.ndarray, slot_of: np.ndarray, topk_w: np.ndarray,
             act_dtype: str, tokens: Optional[Sequence[int]] = None) -> np.ndarray:
-    """out[t] = rnd(sum_j w[t, j] * y_perm[slot_of[t, j]]), summed in pick order.
+    """out[t] = rnd(sum_j w[t, j] * y_perm[slot_of[t, j]]), summed in pick order
+    over the picks that have a row (slot -1: dropped by the gate threshold).
 
     ``y_perm`` holds float64 values of the stored rows.  With ``tokens`` only
     those output rows are computed.
@@ -346,7 +383,11 @@ def combine(y_perm: np.ndarray, slot_of: np.ndarray, topk_w: np.ndarray,
     ts = np.arange(slot_of.shape[0]) if tokens is None else np.asarray(tokens)
     acc = np.zeros((len(ts), y_perm.shape[1]), dtype=np.float64)
     for j in range(slot_of.shape[1]):
-        acc += topk_w[ts, j].astype(np.float64)[:, None] * y_perm[slot_of[ts, j]]
+        sj = slot_of[ts, j]
+        has = sj >= 0
+        if not has.any():
+            continue
+        acc[has] += topk_w[ts[has], j].astype(np.float64)[:, None] * y_perm[sj[has]]
     return round_act(acc, act_dtype)
 
 
@@ -370,6 +411,7 @@ class LayerParams:
     e_begin: int
     e_end: int
     inv_temperature: float = 1.0
+    min_prob: float = 0.0
 
 
 def layer_forward(p: LayerParams, x_stored: np.ndarray,
@@ -390,7 +432,7 @@ def layer_forward(p: LayerParams, x_stored: np.ndarray,
     x64 = decode(x_stored, p.act_dtype)
     if logits is None:
         logits = router_logits(x64, decode(w_router_stored, p.act_dtype))
-    idx, w = route(logits, bias, p.k, p.gate, p.renorm, p.inv_temperature)
+    idx, w = route(logits, bias, p.k, p.gate, p.renorm, p.inv_temperature, p.min_prob)
     counts = expert_counts(idx, p.E)
     offsets = expert_offsets(counts)
     slot_of, row_token = layout_map(idx, offsets)

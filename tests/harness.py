@@ -41,7 +41,8 @@ def params(cfg: LayerConfig) -> O.LayerParams:
     return O.LayerParams(T=cfg.T, H=cfg.H, E=cfg.E, k=cfg.k, I=cfg.I,
                          act_dtype=cfg.act_dtype, w_dtype=cfg.w_dtype, gate=cfg.gate,
                          renorm=cfg.renorm, act=cfg.act, e_begin=cfg.e_begin,
-                         e_end=cfg.e_end, inv_temperature=cfg.inv_temperature)
+                         e_end=cfg.e_end, inv_temperature=cfg.inv_temperature,
+                         min_prob=cfg.min_prob)
 
 
 def spec(cfg: LayerConfig):
@@ -49,7 +50,21 @@ def spec(cfg: LayerConfig):
     return LayerSpec(T=cfg.T, H=cfg.H, E=cfg.E, k=cfg.k, I=cfg.I,
                      act_dtype=TORCH_DTYPE[cfg.act_dtype], gate=cfg.gate,
                      renorm=cfg.renorm, act=cfg.act, e_begin=cfg.e_begin,
-                     e_end=cfg.e_end, inv_temperature=cfg.inv_temperature)
+                     e_end=cfg.e_end, inv_temperature=cfg.inv_temperature,
+                     min_prob=cfg.min_prob)
+
+
+def route(cfg: LayerConfig, logits, bias):
+    """The oracle's top-k gating with the config's flags, after checking that
+    no gate value lies so close to the threshold that float32 rounding could
+    decide it (then the kept set is unique and compared bit for bit)."""
+    if cfg.min_prob > 0:
+        s = O.selection_scores(logits, bias)
+        raw = O.raw_gate(s, O.topk_select(s, cfg.k), cfg.gate, cfg.inv_temperature)
+        gap = np.abs(raw - cfg.min_prob).min()
+        assert gap > 1e-5 * cfg.min_prob, f"a gate value within {gap:.2e} of the threshold"
+    return O.route(logits, bias, cfg.k, cfg.gate, cfg.renorm, cfg.inv_temperature,
+                   cfg.min_prob)
 
 
 def gpu_layer(cfg: LayerConfig, inp, fused=False, split=True):
@@ -85,7 +100,7 @@ def check_routing(cfg, lay, st, check_xperm=True):
     check_xperm=False for the fused kernel, which reads token rows through the
     layout map and writes no permuted copy."""
     logits = lay.logits.cpu().numpy()
-    idx, w = O.route(logits, st["bias"], cfg.k, cfg.gate, cfg.renorm, cfg.inv_temperature)
+    idx, w = route(cfg, logits, st["bias"])
     g_idx = lay.topk_idx.cpu().numpy()
     assert np.array_equal(g_idx, idx), "topk_idx differs"
     assert rel_l2(lay.topk_w.cpu().numpy(), w) <= TOL_F32
@@ -95,7 +110,8 @@ def check_routing(cfg, lay, st, check_xperm=True):
     assert np.array_equal(lay.offsets.cpu().numpy(), offsets)
     slot_of, row_token = O.layout_map(idx, offsets)
     assert np.array_equal(lay.slot_of.cpu().numpy(), slot_of)
-    assert np.array_equal(lay.row_token.cpu().numpy(), row_token)
+    n_kept = int(offsets[-1])      # rows past the kept picks are not written
+    assert np.array_equal(lay.row_token[:n_kept].cpu().numpy(), row_token[:n_kept])
     r0, r1 = int(offsets[cfg.e_begin]), int(offsets[cfg.e_end])
     if check_xperm:
         xp = stored(lay.x_perm[r0:r1])
@@ -106,8 +122,10 @@ def check_routing(cfg, lay, st, check_xperm=True):
 
 def flipped_tokens(cfg, gpu_logits, own_logits, bias):
     """Tokens whose top-k differs between the oracle's own scores and the GPU's."""
-    a, _ = O.route(gpu_logits, bias, cfg.k, cfg.gate, cfg.renorm, cfg.inv_temperature)
-    b, _ = O.route(own_logits, bias, cfg.k, cfg.gate, cfg.renorm, cfg.inv_temperature)
+    a, _ = O.route(gpu_logits, bias, cfg.k, cfg.gate, cfg.renorm, cfg.inv_temperature,
+                   cfg.min_prob)
+    b, _ = O.route(own_logits, bias, cfg.k, cfg.gate, cfg.renorm, cfg.inv_temperature,
+                   cfg.min_prob)
     return np.nonzero((a != b).any(axis=1))[0]
 
 

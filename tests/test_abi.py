@@ -56,11 +56,11 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
 
 def _route(**kw):
     a = dict(x=FAKE, w=FAKE, dt=L.DTYPE_BF16, bias=None, T=4, H=64, E=8, k=2,
-             gate=0, renorm=0, invt=1.0, logits=FAKE, idx=FAKE, w_out=FAKE)
+             gate=0, renorm=0, invt=1.0, minp=0.0, logits=FAKE, idx=FAKE, w_out=FAKE)
     a.update(kw)
     return L.lib().moe_route(a["x"], a["w"], a["dt"], a["bias"], a["T"], a["H"], a["E"],
-                             a["k"], a["gate"], a["renorm"], a["invt"], a["logits"],
-                             a["idx"], a["w_out"], None)
+                             a["k"], a["gate"], a["renorm"], a["invt"], a["minp"],
+                             a["logits"], a["idx"], a["w_out"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -71,6 +71,8 @@ def _route(**kw):
     (dict(H=12), L.MOE_ERR_ARG), (dict(logits=None), L.MOE_ERR_ARG),
     (dict(invt=float("nan")), L.MOE_ERR_ARG), (dict(invt=-1.0), L.MOE_ERR_ARG),
     (dict(T=1 << 28, k=8), L.MOE_ERR_ARG),
+    (dict(minp=-0.01), L.MOE_ERR_ARG), (dict(minp=1.5), L.MOE_ERR_ARG),
+    (dict(minp=float("nan")), L.MOE_ERR_ARG), (dict(minp=0.5, T=0), L.MOE_OK),
 ])
 def test_route_validation(kw, code):
     assert _route(**kw) == code

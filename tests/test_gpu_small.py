@@ -16,17 +16,19 @@ from gen.inputs import make_inputs
 from oracle import moe_oracle as O
 from oracle.torch_io import stored
 from tests.harness import TOL_F32, check_routing, full_parity, gpu_layer, np_stored, \
-    rel_l2, say, spec, to_device
+    rel_l2, route, say, spec, to_device
 
 pytestmark = pytest.mark.gpu
 
 
 def small(name, T, H, E, k, I, act_dtype=BF16, w_dtype=None, gate=SOFTMAX, renorm=False,
-          act=SWIGLU, e_begin=0, e_end=None, bias=None, remote=False, seed_off=0):
+          act=SWIGLU, e_begin=0, e_end=None, bias=None, remote=False, seed_off=0,
+          inv_t=1.0, min_prob=0.0):
     return LayerConfig(name, T=T, H=H, E=E, k=k, I=I, act_dtype=act_dtype,
                        w_dtype=w_dtype or act_dtype, gate=gate, renorm=renorm, act=act,
                        e_begin=e_begin, e_end=E if e_end is None else e_end,
-                       seed=BASE_SEED + 100 + seed_off, bias=bias, remote_rows=remote)
+                       seed=BASE_SEED + 100 + seed_off, bias=bias, remote_rows=remote,
+                       inv_temperature=inv_t, min_prob=min_prob)
 
 
 GRID = [
@@ -54,6 +56,24 @@ GRID = [
     small("fp8_large_m", 400, 256, 8, 2, 256, w_dtype=FP8_E4M3, seed_off=15),
     # long K: the GEMMs' sparse last round is split over K (parts of 4+ k-steps)
     small("bf16_ksplit", 300, 2048, 8, 2, 1024, seed_off=18),
+    # gating variants: temperature, and the minimum-probability threshold
+    # (dropped picks: index -1, no row, nothing to combine); the page's
+    # temperature 0.3 with threshold 0.05, renormalised survivors, sigmoid on
+    # an expert-parallel share, fp32, fp8 weights, and a threshold above
+    # every gate value (all picks dropped: empty FFN, zero output)
+    small("bf16_tau03", 400, 256, 16, 4, 128, inv_t=1 / 0.3, seed_off=50),
+    small("bf16_tau2", 400, 256, 16, 4, 128, inv_t=0.5, seed_off=51),
+    small("bf16_threshold", 500, 256, 16, 4, 128, inv_t=1 / 0.3, min_prob=0.05,
+          seed_off=52),
+    small("f16_threshold_renorm", 300, 256, 8, 2, 256, act_dtype=F16, renorm=True,
+          min_prob=0.3, seed_off=53),
+    small("sigmoid_threshold_ep", 200, 256, 64, 6, 128, gate=SIGMOID, e_begin=8,
+          e_end=40, remote=True, min_prob=0.83, seed_off=54),
+    small("f32_threshold", 255, 128, 8, 2, 256, act_dtype=F32, act=GELU, min_prob=0.2,
+          seed_off=55),
+    small("fp8_threshold", 64, 256, 256, 8, 128, w_dtype=FP8_E4M3, gate=SIGMOID,
+          e_end=32, remote=True, min_prob=0.89, seed_off=56),
+    small("all_dropped", 100, 256, 8, 2, 128, min_prob=1.0, seed_off=57),
 ]
 
 
@@ -103,22 +123,28 @@ def test_mass_ties_in_scores():
         assert rel_l2(lay.topk_w.cpu().numpy(), w) <= TOL_F32
 
 
+# (gate, renorm, inverse temperature, threshold) on the same scores
+GATE_CASES = [("softmax", False, 1 / 0.3, 0.0), ("softmax", True, 1.0, 0.0),
+              ("sigmoid", True, 1.0, 0.0), ("softmax", False, 0.0, 0.0),
+              ("softmax", False, 1 / 0.3, 0.05), ("softmax", True, 1.0, 0.04),
+              ("sigmoid", True, 1.0, 0.93), ("sigmoid", False, 1.0, 0.985)]
+
+
 def test_gate_variants_on_given_scores():
     """Temperature, sigmoid and renormalisation on the same scores."""
     from combine_moe_route_02_amd import MoELayer
     g = torch.Generator().manual_seed(5)
     s = torch.randn((300, 64), generator=g) * 2
     bias = torch.randn(64, generator=g)
-    for gate, renorm, invt in [("softmax", False, 1 / 0.3), ("softmax", True, 1.0),
-                               ("sigmoid", True, 1.0), ("softmax", False, 0.0)]:
-        cfg = small("gates", 300, 256, 64, 6, 128, gate=gate, renorm=renorm)
-        cfg = cfg.with_(inv_temperature=invt)
+    for gate, renorm, invt, thr in GATE_CASES:
+        cfg = small("gates", 300, 256, 64, 6, 128, gate=gate, renorm=renorm,
+                    inv_t=invt, min_prob=thr)
         lay = MoELayer(spec(cfg), "cuda")
         lay.logits.copy_(s.cuda())
-        say(f"[gpu] route gate={gate} renorm={renorm} inv_t={invt}")
+        say(f"[gpu] route gate={gate} renorm={renorm} inv_t={invt} min_prob={thr}")
         lay.route_from_logits(bias.cuda())
         torch.cuda.synchronize()
-        idx, w = O.route(s.numpy(), bias.numpy(), 6, gate, renorm, invt)
+        idx, w = route(cfg, s.numpy(), bias.numpy())
         assert np.array_equal(lay.topk_idx.cpu().numpy(), idx)
         assert rel_l2(lay.topk_w.cpu().numpy(), w) <= TOL_F32
 

@@ -245,6 +245,120 @@ def test_renormalised_weights():
         assert np.all(w1 == 1.0)
 
 
+# Minimum-probability threshold (GPT-4 MoE page, section 2.3 stage 2 and the
+# section 4.1 sketch): a pick survives only if its probability is above it.
+
+
+def _py_softmax(row, inv_t):
+    m = max(float(v) for v in row)
+    z = [math.exp((float(v) - m) * inv_t) for v in row]
+    tot = math.fsum(z)
+    return [v / tot for v in z]
+
+
+@pytest.mark.parametrize("inv_t,theta,renorm", [(1 / 0.3, 0.05, False), (1.0, 0.15, True),
+                                                (0.5, 0.12, False), (1 / 0.3, 0.05, True)])
+def test_threshold_brute_force(inv_t, theta, renorm):
+    """Plain Python per token: the k best experts by (score desc, index asc),
+    kept iff their probability is above theta, renormalised over the kept."""
+    r = np.random.default_rng(77)
+    T, E, k = 60, 6, 3
+    s = r.normal(size=(T, E)).astype(np.float32)
+    idx, w = O.route(s, None, k, "softmax", renorm, inv_t, theta)
+    n_drop = 0
+    for t in range(T):
+        p = _py_softmax(s[t], inv_t)
+        order = sorted(range(E), key=lambda e: (-float(s[t, e]), e))[:k]
+        assert all(abs(p[e] - theta) > 1e-9 for e in order)
+        kept = [e for e in order if p[e] > theta]
+        tot = math.fsum(p[e] for e in kept)
+        for j in range(k):
+            if j < len(kept):
+                e = kept[j]
+                assert idx[t, j] == e
+                want = p[e] / tot if renorm else p[e]
+                assert abs(float(w[t, j]) - want) <= 2 ** -23 * want
+            else:
+                assert idx[t, j] == -1 and w[t, j] == 0.0
+        n_drop += k - len(kept)
+    assert 0 < n_drop < T * k      # both outcomes occur
+
+
+def test_threshold_with_k_equal_E_is_the_set_above_it():
+    """k = E: the kept picks are exactly {e : softmax_e > theta} (library
+    softmax), in descending score order, and every other slot is -1."""
+    from scipy.special import softmax
+    r = np.random.default_rng(78)
+    s = r.normal(size=(50, 8)).astype(np.float32)
+    theta = 0.11
+    idx, _ = O.route(s, None, 8, "softmax", False, 1.0, theta)
+    p = softmax(s.astype(np.float64), axis=1)
+    for t in range(50):
+        want = [int(e) for e in np.argsort(-s[t].astype(np.float64), kind="stable")
+                if p[t, e] > theta]
+        got = idx[t].tolist()
+        assert got == want + [-1] * (8 - len(want))
+
+
+def test_threshold_sigmoid_closed_form():
+    s = np.array([[0.0, math.log(3.0), -math.log(3.0)]], np.float32)
+    idx, w = O.route(s, None, 3, "sigmoid", True, 1.0, 0.4)
+    assert idx.tolist() == [[1, 0, -1]]
+    a = 1 / (1 + math.exp(-float(np.float32(math.log(3.0)))))   # 0.75 up to f32 input
+    assert w[0, 0] == np.float32(a / (a + 0.5))
+    assert w[0, 1] == np.float32(0.5 / (a + 0.5)) and w[0, 2] == 0.0
+
+
+def test_threshold_zero_is_off_and_one_drops_every_softmax_pick():
+    r = np.random.default_rng(79)
+    s = r.normal(size=(30, 8)).astype(np.float32)
+    a = O.route(s, None, 3, "softmax", True, 1.0)
+    b = O.route(s, None, 3, "softmax", True, 1.0, 0.0)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    idx, w = O.route(s, None, 3, "softmax", True, 1.0, 1.0)
+    assert np.all(idx == -1) and np.all(w == 0.0)
+    counts = O.expert_counts(idx, 8)
+    off = O.expert_offsets(counts)
+    assert np.all(counts == 0) and np.all(off == 0)
+    slot_of, row_token = O.layout_map(idx, off)
+    assert np.all(slot_of == -1) and np.all(row_token == -1)
+    out = O.combine(np.ones((90, 4)), slot_of, w, O.F32)
+    assert np.all(out == 0.0)
+
+
+def test_dispatch_and_combine_with_dropped_picks():
+    """Counts = bincount of the kept picks; the layout is the stable argsort of
+    the kept (expert, token) pairs; combine adds only kept picks."""
+    r = np.random.default_rng(80)
+    T, E, k, H = 200, 8, 4, 6
+    s = r.normal(size=(T, E)).astype(np.float32)
+    idx, w = O.route(s, None, k, "softmax", False, 1 / 0.3, 0.05)
+    keep = idx >= 0
+    assert 0 < keep.sum() < T * k
+    assert np.all(np.diff(keep.astype(np.int8), axis=1) <= 0)    # dropped = a suffix
+    counts = O.expert_counts(idx, E)
+    assert np.array_equal(counts, np.bincount(idx[keep], minlength=E))
+    off = O.expert_offsets(counts)
+    assert off[E] == keep.sum()
+    slot_of, row_token = O.layout_map(idx, off)
+    tt, jj = np.nonzero(keep)
+    order = np.argsort(idx[tt, jj].astype(np.int64) * T + tt, kind="stable")
+    n = int(keep.sum())
+    assert np.array_equal(row_token[:n], tt[order]) and np.all(row_token[n:] == -1)
+    inv = np.empty(n, np.int64)
+    inv[order] = np.arange(n)
+    assert np.array_equal(slot_of[tt, jj], inv) and np.all(slot_of[~keep] == -1)
+    y = r.normal(size=(T * k, H))
+    out = O.combine(y, slot_of, w, O.F32)
+    for t in range(0, T, 7):
+        for c in range(H):
+            acc = 0.0
+            for j in range(k):
+                if idx[t, j] >= 0:
+                    acc += float(w[t, j]) * y[slot_of[t, j], c]
+            assert out[t, c] == np.float32(acc)
+
+
 # ---------------------------------------------------------------------------
 # Dispatch
 # ---------------------------------------------------------------------------
