@@ -5,7 +5,7 @@ combine over one batch of synthetic tokens, every step through the C ABI of
 libmoe.so on one HIP stream, inputs already resident in HBM.
 
     python bench.py [--steps K] [--warmup W] [--config c2] [--gpus 1]
-                    [--fused] [--temperature T] [--min-prob P]
+                    [--fused] [--temperature T] [--min-prob P] [--fp8-dispatch]
 
 Prints one JSON line: whole-layer tokens/s, plus the dominant kernel's
 roofline (GEMM-1, timed live with HIP events on the launch stream), the
@@ -63,6 +63,9 @@ def parse():
                     help="softmax temperature of the gate (default: the workload's, 1.0)")
     ap.add_argument("--min-prob", type=float, default=0.0,
                     help="minimum-probability threshold of the gate (0: off)")
+    ap.add_argument("--fp8-dispatch", action="store_true",
+                    help="send the dispatched rows as E4M3 codes with a per-row scale "
+                         "into an fp8 x fp8 GEMM-1 (fp8-weight workloads)")
     return ap.parse_args()
 
 
@@ -75,7 +78,11 @@ def gating_of(args):
     if args.min_prob > 0:
         kw["min_prob"] = args.min_prob
         tag.append(f"threshold {args.min_prob:g}")
-    return kw, (" [gate " + ", ".join(tag) + "]") if tag else ""
+    label = (" [gate " + ", ".join(tag) + "]") if tag else ""
+    if args.fp8_dispatch:
+        kw["fp8_dispatch"] = True
+        label += " [fp8 dispatch transport]"
+    return kw, label
 
 
 def source_hash() -> str:
@@ -140,7 +147,9 @@ def main():
     spec = LayerSpec(T=cfg.T, H=cfg.H, E=cfg.E, k=cfg.k, I=cfg.I, act_dtype=tdt,
                      gate=cfg.gate, renorm=cfg.renorm, act=cfg.act, e_begin=cfg.e_begin,
                      e_end=cfg.e_end, inv_temperature=cfg.inv_temperature,
-                     min_prob=cfg.min_prob)
+                     min_prob=cfg.min_prob, fp8_dispatch=cfg.fp8_dispatch)
+    if cfg.fp8_dispatch and (cfg.w_dtype != "e4m3" or args.fused):
+        sys.exit("--fp8-dispatch needs an fp8-weight workload (c5) and the unfused path")
     lay = MoELayer(spec, dev)
     if inp["y_remote"] is not None:
         lay.y_perm.copy_(inp["y_remote"])
@@ -226,7 +235,8 @@ def main():
     H, I, T, k, E = cfg.H, cfg.I, cfg.T, cfg.k, cfg.E
     loc_pick = (idx >= e0) & (idx < e1)
     tok_needed = int(loc_pick.any(axis=1).sum())
-    disp_bytes = (tok_needed * H * ab + rows_loc * H * ab          # gather
+    row_out = (H + 4) if cfg.fp8_dispatch else H * ab              # codes + scale
+    disp_bytes = (tok_needed * H * ab + rows_loc * row_out         # gather
                   + T * k * 4 * 3 + E * 4 * 2)                    # idx in, slot/row out
     n_kept = int((idx >= 0).sum())                                # picks with a row
     comb_bytes = n_kept * H * ab + T * H * ab + T * k * 8         # rows in, out, slot+w
@@ -242,7 +252,7 @@ def main():
     if args.fused:
         flops1 += flops2   # the fused kernel runs both GEMMs (and combine)
     if cfg.w_dtype == "e4m3":
-        bytes1 = wb1 + rows_loc * H * ab + rows_loc * I * ab
+        bytes1 = wb1 + rows_loc * row_out + rows_loc * I * ab
         achieved = bytes1 / (gemm1_ms * 1e6)
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4)}
@@ -253,6 +263,9 @@ def main():
     n_loc = max(1, e1 - e0)
     if args.fused:
         kname = "fused_layer_kernel (GEMM-1 + SwiGLU + GEMM-2 + combine, moe_layer_fused)"
+    elif cfg.fp8_dispatch:
+        kname = "grouped_gemm_fp8s (GEMM-1 + SwiGLU, fp8 activations x fp8 weights, " \
+                "moe_expert_ffn_up_fp8)"
     elif cfg.w_dtype == "e4m3":
         small_m = lay.spec.max_rows / n_loc <= 48
         kname = ("grouped_gemm_fp8s" if small_m else "grouped_gemm_mfma") + \
@@ -276,7 +289,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": DT_NAME[cfg.act_dtype] + ("+e4m3w" if cfg.w_dtype == "e4m3" else ""),
+        "dtype": DT_NAME[cfg.act_dtype] + ("+e4m3w" if cfg.w_dtype == "e4m3" else "")
+        + ("+e4m3a" if cfg.fp8_dispatch else ""),
         "data": "synthetic (seeded generator; random-init weights)",
         "config": {"workload": f"{cfg.name}: {WORKLOAD[cfg.name]}"
                    + (" [fused kernel]" if args.fused else "") + gate_tag, "tokens": T,
@@ -405,7 +419,8 @@ def cpu_baseline(cfg, inp, sample_tokens: int):
     p = O.LayerParams(T=S, H=sub.H, E=sub.E, k=sub.k, I=sub.I, act_dtype=sub.act_dtype,
                       w_dtype=sub.w_dtype, gate=sub.gate, renorm=sub.renorm, act=sub.act,
                       e_begin=sub.e_begin, e_end=sub.e_end,
-                      inv_temperature=sub.inv_temperature, min_prob=sub.min_prob)
+                      inv_temperature=sub.inv_temperature, min_prob=sub.min_prob,
+                      fp8_dispatch=sub.fp8_dispatch)
     yr = st["y_remote"][: S * cfg.k] if st["y_remote"] is not None else None
     t0 = time.perf_counter()
     O.layer_forward(p, st["x"][:S], st["w_router"], st["bias"], st["w13"], st["w2"],

@@ -21,9 +21,9 @@ GATE_SOFTMAX, GATE_SIGMOID = 0, 1
 ACT_SWIGLU, ACT_GELU = 0, 1
 WS_DISPATCH, WS_FFN, WS_FUSED = 0, 1, 2
 
-EXPORTS = ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_up",
-           "moe_expert_ffn_down", "moe_combine", "moe_layer_fused",
-           "moe_workspace_bytes", "moe_status_string"]
+EXPORTS = ["moe_route", "moe_dispatch", "moe_dispatch_fp8", "moe_expert_ffn",
+           "moe_expert_ffn_up", "moe_expert_ffn_up_fp8", "moe_expert_ffn_down",
+           "moe_combine", "moe_layer_fused", "moe_workspace_bytes", "moe_status_string"]
 
 
 class MoeError(RuntimeError):
@@ -38,6 +38,8 @@ P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
     "moe_route": [P, P, I, P, I, I, I, I, I, I, F, F, P, P, P, P],
     "moe_dispatch": [P, I, P, I, I, I, I, I, I, P, P, P, P, P, P, SZ, P],
+    "moe_dispatch_fp8": [P, I, P, I, I, I, I, I, I, P, P, P, P, P, P, P, SZ, P],
+    "moe_expert_ffn_up_fp8": [P, P, P, I, I, I, I, I, I, P, P, P, P],
     "moe_expert_ffn": [P, P, I, I, I, I, I, I, I, P, P, P, P, I, P, P, P, SZ, P],
     "moe_expert_ffn_up": [P, P, I, I, I, I, I, I, I, P, P, I, P, P, SZ, P],
     "moe_expert_ffn_down": [P, I, I, I, I, I, I, P, P, I, P, P, P, SZ, P],
@@ -105,6 +107,23 @@ def moe_dispatch(x, topk_idx, E, e_begin, e_end, counts, offsets, slot_of, row_t
         ptr(x), DTYPE_OF[x.dtype], ptr(topk_idx), T, H, E, k, e_begin, e_end,
         ptr(counts), ptr(offsets), ptr(slot_of), ptr(row_token), ptr(x_perm),
         ptr(ws), ws.numel() * ws.element_size(), stream_handle(stream)))
+
+
+def moe_dispatch_fp8(x, topk_idx, E, e_begin, e_end, counts, offsets, slot_of, row_token,
+                     x_perm_q, x_scale, ws, stream=None):
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    check("moe_dispatch_fp8", lib().moe_dispatch_fp8(
+        ptr(x), DTYPE_OF[x.dtype], ptr(topk_idx), T, H, E, k, e_begin, e_end,
+        ptr(counts), ptr(offsets), ptr(slot_of), ptr(row_token), ptr(x_perm_q),
+        ptr(x_scale), ptr(ws), ws.numel() * ws.element_size(), stream_handle(stream)))
+
+
+def moe_expert_ffn_up_fp8(x_perm_q, x_scale, offsets, H, I, e_begin, e_end, max_rows, act,
+                          w13, w13_scale, h_ws, stream=None):
+    check("moe_expert_ffn_up_fp8", lib().moe_expert_ffn_up_fp8(
+        ptr(x_perm_q), ptr(x_scale), ptr(offsets), H, I, e_begin, e_end, max_rows, act,
+        ptr(w13), ptr(w13_scale), ptr(h_ws), stream_handle(stream)))
 
 
 def _ws(ws):

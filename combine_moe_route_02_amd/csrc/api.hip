@@ -12,7 +12,7 @@ int route_impl(const void* x, const void* w_router, int act_dtype, const float* 
 int dispatch_impl(const void* x, int act_dtype, const int32_t* idx, int T, int H,
                   int E, int k, int e_begin, int e_end, int32_t* counts,
                   int32_t* offsets, int32_t* slot_of, int32_t* row_token,
-                  void* x_perm, void* ws, hipStream_t s);
+                  void* x_perm, float* x_scale, void* ws, hipStream_t s);
 size_t dispatch_ws_bytes(int T, int E);
 int combine_impl(const void* y_perm, const int32_t* slot_of, const float* w,
                  int act_dtype, int T, int H, int k, void* out, hipStream_t s);
@@ -76,7 +76,27 @@ int moe_dispatch(const void* x, int act_dtype, const int32_t* topk_idx, int T, i
   if (T > 0 && e_end > e_begin && !x_perm) return MOE_ERR_ARG;
   if (!ws || ws_bytes < dispatch_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
   return dispatch_impl(x, act_dtype, topk_idx, T, H, E, k, e_begin, e_end, counts,
-                       offsets, slot_of, row_token, x_perm, ws, stream);
+                       offsets, slot_of, row_token, x_perm, nullptr, ws, stream);
+}
+
+int moe_dispatch_fp8(const void* x, int act_dtype, const int32_t* topk_idx, int T, int H,
+                     int E, int k, int e_begin, int e_end, int32_t* counts,
+                     int32_t* offsets, int32_t* slot_of, int32_t* row_token,
+                     void* x_perm_q, float* x_scale, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  if (act_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (T < 0 || H < 1 || E < 1 || E > 1024 || k < 1 || k > E || k > 32)
+    return MOE_ERR_ARG;
+  if (!pairs_fit(T, k)) return MOE_ERR_ARG;
+  if (e_begin < 0 || e_end < e_begin || e_end > E) return MOE_ERR_ARG;
+  if (H % 8) return MOE_ERR_ARG;
+  if (!counts || !offsets) return MOE_ERR_ARG;
+  if (T > 0 && (!x || !topk_idx || !slot_of || !row_token)) return MOE_ERR_ARG;
+  if (T > 0 && e_end > e_begin && (!x_perm_q || !x_scale)) return MOE_ERR_ARG;
+  if (!ws || ws_bytes < dispatch_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
+  return dispatch_impl(x, act_dtype, topk_idx, T, H, E, k, e_begin, e_end, counts,
+                       offsets, slot_of, row_token, x_perm_q,
+                       x_scale ? x_scale : nullptr, ws, stream);
 }
 
 int moe_expert_ffn_up(const void* x_perm, const int32_t* offsets, int act_dtype, int H,
@@ -114,6 +134,41 @@ int moe_expert_ffn_up(const void* x_perm, const int32_t* offsets, int act_dtype,
   a.K = H;
   return launch_grouped_gemm(act_dtype, w_dtype,
                              act == MOE_ACT_SWIGLU ? EPI_SWIGLU : EPI_GELU, a, max_rows,
+                             stream);
+}
+
+int moe_expert_ffn_up_fp8(const void* x_perm_q, const float* x_scale,
+                          const int32_t* offsets, int H, int I, int e_begin, int e_end,
+                          int max_rows, int act, const void* w13, const float* w13_scale,
+                          void* h_ws, hipStream_t stream) {
+  if (act != MOE_ACT_SWIGLU && act != MOE_ACT_GELU) return MOE_ERR_ARG;
+  if (H < 1 || I < 1 || e_begin < 0 || e_end < e_begin || max_rows < 0)
+    return MOE_ERR_ARG;
+  if (e_end == e_begin || max_rows == 0) return MOE_OK;
+  if (!x_perm_q || !x_scale || !offsets || !w13 || !w13_scale || !h_ws) return MOE_ERR_ARG;
+  const int Nb = act == MOE_ACT_SWIGLU ? 2 * I : I;
+  if (H % 128 || I % 128 || Nb % 256) return MOE_ERR_UNSUPPORTED;
+  GemmArgs a{};
+  a.A = x_perm_q;
+  a.lda = H;
+  a.Ascale = x_scale;
+  a.B = w13;
+  a.strideB = (long long)Nb * H;
+  a.ldb = H;
+  a.Bscale = w13_scale;
+  a.strideS = (long long)(Nb / 128) * (H / 128);
+  a.C = h_ws;
+  a.ldc = I;
+  a.offsets = offsets;
+  a.e_begin = e_begin;
+  a.n_groups = e_end - e_begin;
+  a.a_local = 0;
+  a.c_local = 1;
+  a.c_rows = max_rows;
+  a.Nb = Nb;
+  a.I = I;
+  a.K = H;
+  return launch_gemm_fp8_act(act == MOE_ACT_SWIGLU ? EPI_SWIGLU : EPI_GELU, a, max_rows,
                              stream);
 }
 

@@ -279,10 +279,76 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// fp8 transport of the dispatched rows (ThunderEP page, section 3.3: send
+// the activations in 8 bits).  One 256-thread block per token with a local
+// pick: the block reads the bf16 row once for its amax, picks the power-of-
+// two scale 2^e (the smallest with amax <= 448 * 2^e, so the scaling is
+// exact and nothing saturates), then reads the row again (an L2 hit) and
+// writes E4M3 codes of x * 2^-e, 8 bytes per 16-byte chunk, to every local
+// row of the token, plus 2^e as that row's scale.
+template <int KMAX>
+__global__ void __launch_bounds__(256)
+    gather_fp8_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ idx,
+                      const int32_t* __restrict__ slot_of, int T, int k, int e_begin,
+                      int e_end, int nch /* 16-byte bf16 chunks per row */,
+                      uint2* __restrict__ xq, float* __restrict__ xscale) {
+  __shared__ float s_max[4];
+  const int t = (int)blockIdx.x;
+  const int tid = (int)threadIdx.x;
+  long long rows[KMAX];
+  int slots[KMAX];
+  bool loc[KMAX];
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    loc[j] = false;
+    rows[j] = 0;
+    slots[j] = 0;
+    if (j < k) {
+      const int e = idx[(long long)t * k + j];
+      loc[j] = e >= e_begin && e < e_end;
+      slots[j] = slot_of[(long long)t * k + j];
+      rows[j] = (long long)slots[j] * nch;
+      any |= loc[j];
+    }
+  }
+  if (!any) return;  // block-uniform
+  const uint4* src = x + (long long)t * nch;
+  float m = 0.0f;
+  for (int c = tid; c < nch; c += 256) {
+    float f[8];
+    unpack8<MOE_DTYPE_BF16>(src[c], f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+  }
+  m = wave_max(m);
+  if (lane_id() == 0) s_max[tid >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  const int e = e4m3_row_exponent(amax);
+  for (int c = tid; c < nch; c += 256) {
+    float f[8];
+    unpack8<MOE_DTYPE_BF16>(src[c], f);
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i >> 2] |= f32_to_e4m3(ldexpf(f[i], -e)) << (8 * (i & 3));
+    const uint2 q = make_uint2(w[0], w[1]);
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (loc[j]) xq[rows[j] + c] = q;
+  }
+  if (tid == 0) {
+    const float sc = ldexpf(1.0f, e);
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (loc[j]) xscale[slots[j]] = sc;
+  }
+}
+
 int dispatch_impl(const void* x, int act_dtype, const int32_t* idx, int T, int H,
                   int E, int k, int e_begin, int e_end, int32_t* counts,
                   int32_t* offsets, int32_t* slot_of, int32_t* row_token,
-                  void* x_perm, void* ws, hipStream_t s) {
+                  void* x_perm, float* x_scale, void* ws, hipStream_t s) {
   const int n_tiles = (T + TILE - 1) / TILE;
   int32_t* tile_counts = (int32_t*)ws;
   int32_t* tile_base = tile_counts + (size_t)E * (n_tiles > 0 ? n_tiles : 1);
@@ -316,7 +382,16 @@ int dispatch_impl(const void* x, int act_dtype, const int32_t* idx, int T, int H
 #undef MOE_SLOTS
     }
   }
-  if (n_tiles > 0 && e_end > e_begin) {
+  if (n_tiles > 0 && e_end > e_begin && x_scale) {
+    // fp8 transport: x_perm holds E4M3 codes, x_scale one scale per row
+    const int nch = H * 2 / 16;
+#define MOE_GATHER8(KM)                                                        \
+  hipLaunchKernelGGL((gather_fp8_kernel<KM>), dim3(T), dim3(256), 0, s,         \
+                     (const uint4*)x, idx, slot_of, T, k, e_begin, e_end, nch,  \
+                     (uint2*)x_perm, x_scale)
+    MOE_BY_K(MOE_GATHER8);
+#undef MOE_GATHER8
+  } else if (n_tiles > 0 && e_end > e_begin) {
     const int elem = act_dtype == MOE_DTYPE_F32 ? 4 : 2;
     const int nch = H * elem / 16;
     int slices, cps;

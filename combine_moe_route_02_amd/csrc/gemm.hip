@@ -294,16 +294,26 @@ __device__ __forceinline__ bf16x8 decode_fp8x8(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
-template <int DT, int EPI>
+// A8: the activations arrive as E4M3 codes with one power-of-two scale per
+// row (fp8 dispatch transport).  Both operands then stay fp8 from HBM to the
+// MFMA (v_mfma_f32_32x32x16_fp8_fp8, same fragment layout as the 16-bit
+// 32x32x16 form, one byte per element); the row scale multiplies the fp32
+// sums in the epilogue (exact: a power of two).
+__device__ __forceinline__ long fp8x8_as_long(uint32_t lo, uint32_t hi) {
+  return (long)(((unsigned long)hi << 32) | lo);
+}
+
+template <int DT, int EPI, bool A8 = false>
 struct Fp8SmallTile {
   static_assert(DT == MOE_DTYPE_BF16, "fp8 weights pair with bf16 activations");
   static constexpr int BM = 32, BN = 256, BK = 128, NS = 3, NW = 4;
   static constexpr int NT = NW * 64;
   static constexpr int TN = 2;                        // 32-column groups per wave
-  static constexpr int A_ROWB = BK * 2, B_ROWB = BK;  // 256 B (16-bit), 128 B (fp8)
+  static constexpr int A_ROWB = A8 ? BK : BK * 2;     // 128 B (fp8) or 256 B (16-bit)
+  static constexpr int B_ROWB = BK;                   // 128 B (fp8)
   static constexpr int A_BYTES = BM * A_ROWB, B_BYTES = BN * B_ROWB;
   static constexpr int STAGE = A_BYTES + B_BYTES;     // 40 KB
-  static constexpr int A_BLK = A_BYTES / 1024;        // blocks of 4 A rows
+  static constexpr int A_BLK = A_BYTES / 1024;        // blocks of 4 (fp8: 8) A rows
   static constexpr int B_BLK = B_BYTES / 1024;        // blocks of 8 B rows
   static constexpr int BPW = (A_BLK + B_BLK) / NW;
   static constexpr int JA = A_BLK / NW;
@@ -325,7 +335,8 @@ struct Fp8SmallTile {
 
     int base_row = ti.r0 - a_sub;
     if (p.a_local && base_row > p.a_rows - 1) base_row = p.a_rows - 1;
-    const char* a_tile = uniform_ptr((const char*)p.A + (long long)base_row * p.lda * 2);
+    constexpr int AE = A8 ? 1 : 2;  // bytes per A element
+    const char* a_tile = uniform_ptr((const char*)p.A + (long long)base_row * p.lda * AE);
     const char* b_tile = uniform_ptr((const char*)p.B + (long long)ti.g * p.strideB);
     uint32_t voff[BPW];
     int ldsoff[BPW];
@@ -333,14 +344,15 @@ struct Fp8SmallTile {
     for (int j = 0; j < BPW; ++j) {
       const int q = wn + NW * j;
       if (j < JA) {
-        // A: 4 rows x 256 B per block; 16-byte chunk c of row r at c ^ (r & 15)
-        const int row = 4 * q + (lane >> 4);
-        const int kc = (lane & 15) ^ (row & 15);
+        // 16-bit A: 4 rows x 256 B per block, 16-byte chunk c of row r at
+        // c ^ (r & 15); fp8 A: 8 rows x 128 B, chunk c at c ^ ((r >> 1) & 7)
+        const int row = A8 ? 8 * q + (lane >> 3) : 4 * q + (lane >> 4);
+        const int kc = A8 ? (lane & 7) ^ ((row >> 1) & 7) : (lane & 15) ^ (row & 15);
         int grow = ti.r0 + row;
         grow = grow < ti.r1 ? grow : ti.r1 - 1;
         int arow = grow - a_sub;
         if (p.a_local && arow >= p.a_rows) arow = p.a_rows - 1;
-        voff[j] = (uint32_t)(arow - base_row) * (uint32_t)(p.lda * 2) + (uint32_t)(kc * 16);
+        voff[j] = (uint32_t)(arow - base_row) * (uint32_t)(p.lda * AE) + (uint32_t)(kc * 16);
         ldsoff[j] = q * 1024;
       } else {
         // B: 8 rows x 128 B per block; 16-byte chunk c of row r at c ^ ((r >> 1) & 7)
@@ -408,13 +420,27 @@ do {                                                                            
         for (int v = 0; v < 16; ++v) part[j][v] = 0.0f;
 #pragma unroll
       for (int s8 = 0; s8 < BK / 16; ++s8) {
-        const V a = *(const V*)(As + lrow * A_ROWB + (((2 * s8 + khalf) ^ (lrow & 15)) << 4));
+        if constexpr (A8) {
+          const uint2 a8 = *(const uint2*)(As + lrow * A_ROWB +
+                                          ((s8 ^ ((lrow >> 1) & 7)) << 4) + khalf * 8);
+          const long a = fp8x8_as_long(a8.x, a8.y);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int brow = wn * 64 + j * 32 + lrow;
-          const uint2 q8 = *(const uint2*)(Bs + brow * B_ROWB +
-                                          ((s8 ^ ((brow >> 1) & 7)) << 4) + khalf * 8);
-          part[j] = MfmaOp<DT>::run(a, decode_fp8x8(q8.x, q8.y), part[j]);
+          for (int j = 0; j < TN; ++j) {
+            const int brow = wn * 64 + j * 32 + lrow;
+            const uint2 q8 = *(const uint2*)(Bs + brow * B_ROWB +
+                                            ((s8 ^ ((brow >> 1) & 7)) << 4) + khalf * 8);
+            part[j] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(
+                a, fp8x8_as_long(q8.x, q8.y), part[j], 0, 0, 0);
+          }
+        } else {
+          const V a = *(const V*)(As + lrow * A_ROWB + (((2 * s8 + khalf) ^ (lrow & 15)) << 4));
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int brow = wn * 64 + j * 32 + lrow;
+            const uint2 q8 = *(const uint2*)(Bs + brow * B_ROWB +
+                                            ((s8 ^ ((brow >> 1) & 7)) << 4) + khalf * 8);
+            part[j] = MfmaOp<DT>::run(a, decode_fp8x8(q8.x, q8.y), part[j]);
+          }
         }
       }
 #pragma unroll
@@ -431,6 +457,11 @@ do {                                                                            
       if (grow >= ti.r1) continue;
       const long long crow = grow - c_sub;
       if (p.c_local && crow >= p.c_rows) continue;
+      if constexpr (A8) {
+        const float as = p.Ascale[grow - a_sub];  // the row's power-of-two scale
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[j][v] *= as;
+      }
       uint16_t* C = (uint16_t*)p.C;
       if (EPI == EPI_SWIGLU) {
         const float h = silu_mul(acc[0][v], acc[1][v]);
@@ -447,9 +478,9 @@ do {                                                                            
   }
 };
 
-template <int DT, int EPI>
+template <int DT, int EPI, bool A8 = false>
 __global__ void __launch_bounds__(256) grouped_gemm_fp8s(GemmArgs p) {
-  typedef Fp8SmallTile<DT, EPI> Tile;
+  typedef Fp8SmallTile<DT, EPI, A8> Tile;
   __shared__ __attribute__((aligned(1024))) char smem[Tile::SMEM];
   __shared__ int s_pre[1024];
   __shared__ int s_scan[Tile::NT];
@@ -690,12 +721,12 @@ int run_dma(GemmArgs a, int max_rows, int gm, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
-template <int DT, int EPI>
+template <int DT, int EPI, bool A8 = false>
 int run_fp8s(GemmArgs a, int max_rows, hipStream_t s) {
   if (a.Nb % 256 || a.K % 128) return MOE_ERR_UNSUPPORTED;
   if ((long long)a.Nb * a.ldb >= (1ll << 32)) return MOE_ERR_UNSUPPORTED;
   if (a.offsets && a.n_groups > 1024) return MOE_ERR_UNSUPPORTED;
-  auto kern = grouped_gemm_fp8s<DT, EPI>;
+  auto kern = grouped_gemm_fp8s<DT, EPI, A8>;
   const dim3 grid = persistent_grid(kern, 256, a, max_rows, 32, 256, 1);
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
@@ -777,6 +808,16 @@ int by_epi(int epi, GemmArgs a, int max_rows, hipStream_t s) {
 }
 
 }  // namespace
+
+int launch_gemm_fp8_act(int epi, GemmArgs a, int max_rows, hipStream_t stream) {
+  // every row count runs on the 32-row tile: the fp8 transport serves the
+  // weight-streaming decode regime
+  switch (epi) {
+    case EPI_SWIGLU: return run_fp8s<MOE_DTYPE_BF16, EPI_SWIGLU, true>(a, max_rows, stream);
+    case EPI_GELU: return run_fp8s<MOE_DTYPE_BF16, EPI_GELU, true>(a, max_rows, stream);
+  }
+  return MOE_ERR_ARG;
+}
 
 int launch_grouped_gemm(int act_dtype, int w_dtype, int epi, GemmArgs a,
                         int max_rows, hipStream_t stream) {

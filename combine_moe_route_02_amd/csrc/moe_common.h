@@ -57,6 +57,39 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
   return (code & 0x80u) ? -v : v;
 }
 
+// float32 -> OCP E4M3FN code, round to nearest even, for |v| <= 448 (the
+// caller's scaling guarantees it; nothing saturates).  The sign bit is kept,
+// so -0 and negative values that round to zero give 0x80.  Below the
+// smallest normal (2^-6) the code is the integer nearest v * 2^9 (exact
+// product; 8 carries into the smallest normal); above it the 23-bit binary32
+// mantissa is rounded to 3 bits, a carry out of the mantissa stepping the
+// exponent field.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t a = b & 0x7fffffffu;
+  uint32_t code;
+  if (a < 0x3c800000u) {  // |v| < 2^-6
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  } else {
+    const uint32_t e = (a >> 23) - 120u;  // biased exponent 127 -> 7
+    const uint32_t keep = (a >> 20) & 7u, rem = a & 0xfffffu;
+    const uint32_t up = (rem > 0x80000u) || (rem == 0x80000u && (keep & 1u));
+    code = (e << 3) + keep + up;
+  }
+  return code | sign;
+}
+
+// Power-of-two scale exponent of an fp8 row: the smallest e with
+// amax <= 448 * 2^e (448 = 0.875 * 2^9 is E4M3's largest finite value), so
+// every |x| * 2^-e fits without saturation; 0 for an all-zero row.
+__device__ __forceinline__ int e4m3_row_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int ex;
+  const float m = frexpf(amax, &ex);  // amax = m * 2^ex, m in [0.5, 1)
+  return ex - 9 + (m > 0.875f ? 1 : 0);
+}
+
 template <int DT> struct Act;
 template <> struct Act<MOE_DTYPE_F32> {
   typedef float T;
@@ -102,6 +135,12 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, MOE_WAVE));
   return v;
 }
 

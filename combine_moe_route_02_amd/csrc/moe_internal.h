@@ -10,8 +10,9 @@ enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_GELU = 2, EPI_F32 = 3 };
 // One grouped GEMM  C[r, n] = epi( sum_k A[r, k] * B_g[n', k] )  over the
 // row segments of groups g = 0..n_groups-1.
 struct GemmArgs {
-  const void* A;          // activations, 16-bit or f32
+  const void* A;          // activations, 16-bit or f32 (E4M3 codes: launch_gemm_fp8_act)
   long long lda;
+  const float* Ascale;    // E4M3 activations: one scale per A row
   const void* B;          // weights of group 0; group g at B + g * strideB
   long long strideB;      // elements (bytes for fp8)
   long long ldb;
@@ -62,5 +63,8 @@ inline void row_slices(int T, int nch, int& slices, int& cps) {
 // GEMM launchers; return MOE_OK / MOE_ERR_UNSUPPORTED / MOE_ERR_HIP.
 int launch_grouped_gemm(int act_dtype, int w_dtype, int epi, GemmArgs a,
                         int max_rows, hipStream_t stream);
+// E4M3 activations (per-row scales) times E4M3 weights (128x128 block
+// scales) on fp8 MFMA, bf16 output.
+int launch_gemm_fp8_act(int epi, GemmArgs a, int max_rows, hipStream_t stream);
 
 }  // namespace moe

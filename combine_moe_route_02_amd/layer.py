@@ -32,6 +32,7 @@ class LayerSpec:
     e_end: int = -1          # -1: all experts are local
     inv_temperature: float = 1.0
     min_prob: float = 0.0    # gate threshold; 0 = off
+    fp8_dispatch: bool = False   # send dispatched rows as E4M3 codes (fp8 weights)
 
     @property
     def local(self):
@@ -58,7 +59,13 @@ class MoELayer:
         self.offsets = torch.empty((s.E + 1,), **i32)
         self.slot_of = torch.empty((s.T, s.k), **i32)
         self.row_token = torch.empty((N,), **i32)
-        self.x_perm = torch.empty((N, s.H), dtype=s.act_dtype, device=dev)
+        # fp8 transport: E4M3 codes and one scale per row instead of x_perm
+        self.x_perm = torch.empty((1 if s.fp8_dispatch else N, s.H), dtype=s.act_dtype,
+                                  device=dev)
+        self.x_q = self.x_scale = None
+        if s.fp8_dispatch:
+            self.x_q = torch.empty((N, s.H), dtype=torch.uint8, device=dev)
+            self.x_scale = torch.empty((max(N, 1),), dtype=torch.float32, device=dev)
         self.h = torch.empty((max(s.max_rows, 1), s.I), dtype=s.act_dtype, device=dev)
         self.y_perm = torch.zeros((N, s.H), dtype=s.act_dtype, device=dev)
         self.out = torch.empty((s.T, s.H), dtype=s.act_dtype, device=dev)
@@ -88,12 +95,22 @@ class MoELayer:
     def dispatch(self, x, stream=None):
         s = self.spec
         e0, e1 = s.local
+        if s.fp8_dispatch:
+            L.moe_dispatch_fp8(x, self.topk_idx, s.E, e0, e1, self.counts, self.offsets,
+                               self.slot_of, self.row_token, self.x_q, self.x_scale,
+                               self.ws, stream=stream)
+            return
         L.moe_dispatch(x, self.topk_idx, s.E, e0, e1, self.counts, self.offsets,
                        self.slot_of, self.row_token, self.x_perm, self.ws, stream=stream)
 
     def ffn_up(self, w13, w13_scale=None, stream=None):
         s = self.spec
         e0, e1 = s.local
+        if s.fp8_dispatch:
+            L.moe_expert_ffn_up_fp8(self.x_q, self.x_scale, self.offsets, s.H, s.I, e0, e1,
+                                    s.max_rows, ACTS[s.act], w13, w13_scale, self.h,
+                                    stream=stream)
+            return
         L.moe_expert_ffn_up(self.x_perm, self.offsets, s.H, s.I, e0, e1, s.max_rows,
                             ACTS[s.act], w13, w13_scale, self.h, ws=self.ws_ffn,
                             stream=stream)
@@ -107,6 +124,10 @@ class MoELayer:
     def ffn(self, w13, w2, w13_scale=None, w2_scale=None, stream=None):
         s = self.spec
         e0, e1 = s.local
+        if s.fp8_dispatch:
+            self.ffn_up(w13, w13_scale, stream)
+            self.ffn_down(w2, w2_scale, stream)
+            return
         L.moe_expert_ffn(self.x_perm, self.offsets, s.H, s.I, e0, e1, s.max_rows,
                          ACTS[s.act], w13, w13_scale, w2, w2_scale, self.h, self.y_perm,
                          ws=self.ws_ffn, stream=stream)

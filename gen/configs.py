@@ -51,6 +51,7 @@ class LayerConfig:
     remote_rows: bool = False      # pre-filled "received" rows for non-local experts
     inv_temperature: float = 1.0
     min_prob: float = 0.0          # gate threshold (0: off)
+    fp8_dispatch: bool = False     # dispatched rows travel as E4M3 + per-row scale
 
     @property
     def E_loc(self) -> int:

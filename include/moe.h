@@ -131,6 +131,51 @@ int moe_dispatch(const void* x, int act_dtype, const int32_t* topk_idx,
                  hipStream_t stream);
 
 /*
+ * moe_dispatch_fp8 - moe_dispatch with the gathered rows sent in 8 bits.
+ *
+ * Defines: dispatch transport in FP8 (ThunderEP page, section 3.3: the
+ * dispatched activations travel as 8-bit floats, halving the bytes).  Each
+ * token's row gets one power-of-two scale 2^e, the smallest with
+ * max_h |x[t][h]| <= 448 * 2^e (0 for an all-zero row), so x * 2^-e is exact
+ * and never saturates; the codes are OCP E4M3FN, round to nearest even.
+ *
+ * Arguments as moe_dispatch (act_dtype must be MOE_DTYPE_BF16), except:
+ *  x_perm_q   [T*k][H] uint8 output: E4M3 codes of x[row_token[r]] * 2^-e,
+ *             rows of local experts only.
+ *  x_scale    [T*k] float32 output: 2^e of each local row.
+ * Counts, offsets, slot_of and row_token are those of moe_dispatch.
+ */
+int moe_dispatch_fp8(const void* x, int act_dtype, const int32_t* topk_idx,
+                     int T, int H, int E, int k, int e_begin, int e_end,
+                     int32_t* counts, int32_t* offsets, int32_t* slot_of,
+                     int32_t* row_token, void* x_perm_q, float* x_scale, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_expert_ffn_up_fp8 - GEMM-1 + activation on fp8-transported rows.
+ *
+ * Defines: the expert's first Linear and activation (GPT-4 MoE page,
+ * section 3.1 table; SwiGLU's two projections) with both operands in fp8,
+ * the ThunderEP page's section 3.3 transport feeding the matrix units
+ * directly.  h[r] = act(x_scale[r] * sum_k q[r][k] * W13[n][k]), where
+ * W13 = decode(w13) * w13_scale block-wise as for MOE_DTYPE_FP8_E4M3
+ * weights; products accumulate in float32 per 128-wide k block, the block
+ * scale multiplies each block's sum and the row scale the total.
+ *
+ *  x_perm_q, x_scale  from moe_dispatch_fp8 (global row numbering).
+ *  w13, w13_scale     E4M3 weights and their 128x128 block scales, as for
+ *                     moe_expert_ffn with w_dtype MOE_DTYPE_FP8_E4M3.
+ *  h_ws               [max_rows][I] bf16 output, row r - offsets[e_begin].
+ * Limits: H % 128 == 0, I % 128 == 0 (MOE_ERR_UNSUPPORTED otherwise).  The
+ * 32-row tile serves every row count (it is built for decode batches).
+ * GEMM-2 and combine are moe_expert_ffn_down and moe_combine, unchanged.
+ */
+int moe_expert_ffn_up_fp8(const void* x_perm_q, const float* x_scale,
+                          const int32_t* offsets, int H, int I, int e_begin,
+                          int e_end, int max_rows, int act, const void* w13,
+                          const float* w13_scale, void* h_ws, hipStream_t stream);
+
+/*
  * moe_expert_ffn - grouped expert FFN over the local experts' rows.
  *
  * Defines: each expert is an FFN, Linear -> activation -> Linear (GPT-4 MoE

@@ -142,6 +142,59 @@ def e4m3_decode(bits: np.ndarray) -> np.ndarray:
     return s * val
 
 
+E4M3_MAX = 448.0
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """float64 -> OCP E4M3FN codes, round to nearest even, saturating to +-448.
+
+    Written from the format: 4 significant bits, smallest normal exponent -6
+    (subnormals are multiples of 2**-9), largest finite 1.75 * 2**8 = 448
+    (the pattern S.1111.111 is NaN).  The sign bit follows the input's sign,
+    so -0.0 and negative values that round to zero give 0x80.  NaN -> 0x7F.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, ex = np.frexp(a)                       # a = m * 2**ex, m in [0.5, 1)
+    e = np.maximum(ex - 1, -6)                # exponent, clamped at the subnormal range
+    q = np.ldexp(1.0, e - 3)                  # spacing of E4M3 values near a
+    r = np.minimum(np.round(a / q) * q, E4M3_MAX)   # np.round: halves to even
+    sub = r < 2.0 ** -6
+    _, er = np.frexp(np.where(sub, 1.0, r))
+    E = er - 1                                # exponent of a normal result
+    mant = np.where(sub, 0, np.round(np.ldexp(r, -E) * 8.0) - 8.0)
+    code = np.where(sub, np.round(np.ldexp(r, 9)), ((E + 7) << 3) + mant)
+    code = code.astype(np.int64) | (np.signbit(x).astype(np.int64) << 7)
+    code = np.where(np.isnan(x), 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def e4m3_row_exponent(amax) -> np.ndarray:
+    """Smallest integer e with amax <= 448 * 2**e (0 where amax == 0).
+
+    448 = 0.875 * 2**9 and amax = m * 2**ex with m in [0.5, 1), so
+    e = ex - 9, plus one when m > 0.875; exact, no logarithms.
+    """
+    amax = np.asarray(amax, dtype=np.float64)
+    m, ex = np.frexp(amax)
+    e = ex - 9 + (m > 0.875)
+    return np.where(amax > 0, e, 0).astype(np.int64)
+
+
+def quantize_rows_e4m3(x: np.ndarray):
+    """fp8 transport of activation rows (ThunderEP page, section 3.3: send the
+    dispatched activations as 8-bit floats with a dynamic scale).  Each row
+    gets the power-of-two scale 2**e of e4m3_row_exponent(max |x|), so that
+    x * 2**-e is exact and within +-448; codes are e4m3_encode of it.
+
+    Returns (codes uint8 [R, H], scales float32 [R] = 2**e).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    e = e4m3_row_exponent(np.abs(x).max(axis=1) if x.shape[1] else np.zeros(len(x)))
+    codes = e4m3_encode(np.ldexp(x, -e[:, None]))
+    return codes, np.ldexp(1.0, e).astype(np.float32)
+
+
 def decode(arr: np.ndarray, dtype: str) -> np.ndarray:
     """Stored tensor (bits for 16/8-bit formats, float32 values) -> float64."""
     if dtype == F32:
@@ -412,6 +465,7 @@ class LayerParams:
     e_end: int
     inv_temperature: float = 1.0
     min_prob: float = 0.0
+    fp8_dispatch: bool = False   # rows sent as E4M3 codes with a per-row scale
 
 
 def layer_forward(p: LayerParams, x_stored: np.ndarray,
@@ -438,13 +492,19 @@ def layer_forward(p: LayerParams, x_stored: np.ndarray,
     slot_of, row_token = layout_map(idx, offsets)
     r0, r1 = int(offsets[p.e_begin]), int(offsets[p.e_end])
     x_perm = gather_rows(x_stored, row_token, r0, r1)
+    x_scale = None
+    if p.fp8_dispatch:
+        # the expert FFN sees the dequantised rows: code value * row scale
+        x_perm, x_scale = quantize_rows_e4m3(decode(x_perm, p.act_dtype))
+        xp64 = e4m3_decode(x_perm) * x_scale.astype(np.float64)[:, None]
+    else:
+        xp64 = decode(x_perm, p.act_dtype)
 
     N = p.T * p.k
     if y_remote_stored is not None:
         y_perm = decode(y_remote_stored, p.act_dtype).copy()
     else:
         y_perm = np.zeros((N, p.H), dtype=np.float64)
-    xp64 = decode(x_perm, p.act_dtype)
     for el in range(p.e_end - p.e_begin):
         e = p.e_begin + el
         a, b = int(offsets[e]) - r0, int(offsets[e + 1]) - r0
@@ -455,7 +515,7 @@ def layer_forward(p: LayerParams, x_stored: np.ndarray,
     out = combine(y_perm, slot_of, w, p.act_dtype)
     return dict(logits=logits, topk_idx=idx, topk_w=w, counts=counts,
                 offsets=offsets, slot_of=slot_of, row_token=row_token,
-                x_perm=x_perm, y_perm=y_perm, out=out)
+                x_perm=x_perm, x_scale=x_scale, y_perm=y_perm, out=out)
 
 
 def expert_weights(p: LayerParams, w13_stored, w2_stored, w13_scale, w2_scale,

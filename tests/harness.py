@@ -42,7 +42,7 @@ def params(cfg: LayerConfig) -> O.LayerParams:
                          act_dtype=cfg.act_dtype, w_dtype=cfg.w_dtype, gate=cfg.gate,
                          renorm=cfg.renorm, act=cfg.act, e_begin=cfg.e_begin,
                          e_end=cfg.e_end, inv_temperature=cfg.inv_temperature,
-                         min_prob=cfg.min_prob)
+                         min_prob=cfg.min_prob, fp8_dispatch=cfg.fp8_dispatch)
 
 
 def spec(cfg: LayerConfig):
@@ -51,7 +51,7 @@ def spec(cfg: LayerConfig):
                      act_dtype=TORCH_DTYPE[cfg.act_dtype], gate=cfg.gate,
                      renorm=cfg.renorm, act=cfg.act, e_begin=cfg.e_begin,
                      e_end=cfg.e_end, inv_temperature=cfg.inv_temperature,
-                     min_prob=cfg.min_prob)
+                     min_prob=cfg.min_prob, fp8_dispatch=cfg.fp8_dispatch)
 
 
 def route(cfg: LayerConfig, logits, bias):
@@ -113,7 +113,13 @@ def check_routing(cfg, lay, st, check_xperm=True):
     n_kept = int(offsets[-1])      # rows past the kept picks are not written
     assert np.array_equal(lay.row_token[:n_kept].cpu().numpy(), row_token[:n_kept])
     r0, r1 = int(offsets[cfg.e_begin]), int(offsets[cfg.e_end])
-    if check_xperm:
+    if check_xperm and cfg.fp8_dispatch:
+        # fp8 transport: codes and power-of-two scales are exact, bit for bit
+        rows = O.decode(O.gather_rows(st["x"], row_token, r0, r1), cfg.act_dtype)
+        codes, scales = O.quantize_rows_e4m3(rows)
+        assert np.array_equal(lay.x_q[r0:r1].cpu().numpy(), codes), "x_q differs"
+        assert np.array_equal(lay.x_scale[r0:r1].cpu().numpy(), scales), "x_scale differs"
+    elif check_xperm:
         xp = stored(lay.x_perm[r0:r1])
         assert np.array_equal(xp, O.gather_rows(st["x"], row_token, r0, r1)), "x_perm differs"
     return dict(logits=logits, idx=idx, w=w, counts=counts, offsets=offsets,

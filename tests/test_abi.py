@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "moe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary_calls():
@@ -129,6 +129,29 @@ def test_ffn_validation():
     assert lib.moe_expert_ffn_down(FAKE, L.DTYPE_BF16, 256, 128, 0, 8, 64, FAKE, None,
                                    L.DTYPE_BF16, FAKE, FAKE, FAKE, 100,
                                    None) == L.MOE_ERR_WORKSPACE
+
+
+def test_fp8_transport_validation():
+    lib = L.lib()
+    d = lib.moe_dispatch_fp8
+    args = [FAKE, L.DTYPE_BF16, FAKE, 4, 64, 8, 2, 0, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+            FAKE, 1 << 20, None]
+    def call(i, v):
+        a = list(args)
+        a[i] = v
+        return d(*a)
+    assert call(1, L.DTYPE_F16) == L.MOE_ERR_UNSUPPORTED      # bf16 rows only
+    assert call(14, None) == L.MOE_ERR_ARG                    # no scale output
+    assert call(13, None) == L.MOE_ERR_ARG                    # no code output
+    assert call(4, 60) == L.MOE_ERR_ARG                       # H % 8
+    assert call(16, 8) == L.MOE_ERR_WORKSPACE
+    u = lib.moe_expert_ffn_up_fp8
+    assert u(FAKE, FAKE, FAKE, 192, 128, 0, 8, 64, 0, FAKE, FAKE, FAKE, None) == \
+        L.MOE_ERR_UNSUPPORTED                                 # H % 128
+    assert u(FAKE, None, FAKE, 256, 128, 0, 8, 64, 0, FAKE, FAKE, FAKE, None) == L.MOE_ERR_ARG
+    assert u(FAKE, FAKE, FAKE, 256, 128, 0, 8, 64, 0, FAKE, None, FAKE, None) == L.MOE_ERR_ARG
+    assert u(FAKE, FAKE, FAKE, 256, 128, 0, 8, 64, 7, FAKE, FAKE, FAKE, None) == L.MOE_ERR_ARG
+    assert u(FAKE, FAKE, FAKE, 256, 128, 3, 3, 64, 0, FAKE, FAKE, FAKE, None) == L.MOE_OK
 
 
 def test_combine_and_fused_validation():

@@ -47,7 +47,7 @@ def sampled_parity(cfg, inp, lay, n_tokens=48, seed=7, check_xperm=True):
 
     # rows to check: the sampled tokens' picks + each local segment's ends
     off, slot_of, idx = r["offsets"], r["slot_of"], r["idx"]
-    rows = set(slot_of[toks].ravel().tolist())
+    rows = set(r_ for r_ in slot_of[toks].ravel().tolist() if r_ >= 0)   # -1: dropped
     for e in range(cfg.e_begin, cfg.e_end):
         if off[e + 1] > off[e]:
             rows.update([int(off[e]), int(off[e + 1]) - 1])
@@ -72,6 +72,9 @@ def sampled_parity(cfg, inp, lay, n_tokens=48, seed=7, check_xperm=True):
         s2 = stored(inp["w2_scale"][el])[None] if inp["w2_scale"] is not None else None
         W13, W2 = O.expert_weights(p, w13[None], w2[None], s13, s2, 0)
         X = O.decode(st["x"][r["row_token"][rows[sel]]], cfg.act_dtype)
+        if cfg.fp8_dispatch:      # the FFN sees the dequantised fp8 rows
+            codes, sc = O.quantize_rows_e4m3(X)
+            X = O.e4m3_decode(codes) * sc.astype(np.float64)[:, None]
         y_ref[sel] = O.expert_ffn(X, W13, W2, cfg.act, cfg.act_dtype)
     loc = np.nonzero(local_sel)[0]
     if len(loc):
@@ -83,7 +86,7 @@ def sampled_parity(cfg, inp, lay, n_tokens=48, seed=7, check_xperm=True):
 
     # combine of sampled tokens, from the oracle's rows
     pos = {int(rw): i for i, rw in enumerate(rows)}
-    slot_c = np.vectorize(pos.get)(slot_of[toks]).astype(np.int64)
+    slot_c = np.vectorize(lambda r_: pos.get(r_, -1))(slot_of[toks]).astype(np.int64)
     out_ref = O.combine(y_ref, slot_c, r["w"][toks], cfg.act_dtype,
                         tokens=np.arange(len(toks)))
     out_gpu = O.decode(stored(lay.out[torch.as_tensor(toks, device="cuda")]), cfg.act_dtype)
@@ -106,3 +109,13 @@ def test_full_size_config(name):
         say(f"  c4 load max/mean {ratio:.2f}, local rows "
             f"{int(r['offsets'][cfg.e_end] - r['offsets'][cfg.e_begin])}")
         assert abs(ratio - 10.0) < 0.5
+
+
+def test_c5_fp8_dispatch():
+    """The decode layer with its dispatched rows sent as E4M3 (fp8 x fp8 GEMM-1):
+    codes and scales bit-exact, outputs against the oracle's fp8 transport."""
+    cfg = CONFIGS["c5"].with_(fp8_dispatch=True)
+    say("[gen] c5 (fp8 dispatch) on cuda")
+    inp = make_inputs(cfg, "cuda")
+    lay = gpu_layer(cfg, inp)
+    sampled_parity(cfg, inp, lay, n_tokens=64)

@@ -16,19 +16,19 @@ from gen.inputs import make_inputs
 from oracle import moe_oracle as O
 from oracle.torch_io import stored
 from tests.harness import TOL_F32, check_routing, full_parity, gpu_layer, np_stored, \
-    rel_l2, route, say, spec, to_device
+    params, rel_l2, route, say, spec, to_device
 
 pytestmark = pytest.mark.gpu
 
 
 def small(name, T, H, E, k, I, act_dtype=BF16, w_dtype=None, gate=SOFTMAX, renorm=False,
           act=SWIGLU, e_begin=0, e_end=None, bias=None, remote=False, seed_off=0,
-          inv_t=1.0, min_prob=0.0):
+          inv_t=1.0, min_prob=0.0, fp8d=False):
     return LayerConfig(name, T=T, H=H, E=E, k=k, I=I, act_dtype=act_dtype,
                        w_dtype=w_dtype or act_dtype, gate=gate, renorm=renorm, act=act,
                        e_begin=e_begin, e_end=E if e_end is None else e_end,
                        seed=BASE_SEED + 100 + seed_off, bias=bias, remote_rows=remote,
-                       inv_temperature=inv_t, min_prob=min_prob)
+                       inv_temperature=inv_t, min_prob=min_prob, fp8_dispatch=fp8d)
 
 
 GRID = [
@@ -74,6 +74,17 @@ GRID = [
     small("fp8_threshold", 64, 256, 256, 8, 128, w_dtype=FP8_E4M3, gate=SIGMOID,
           e_end=32, remote=True, min_prob=0.89, seed_off=56),
     small("all_dropped", 100, 256, 8, 2, 128, min_prob=1.0, seed_off=57),
+    # fp8 dispatch transport: E4M3 rows with a power-of-two scale per row into
+    # the fp8 x fp8 GEMM-1 (decode batch on an EP share, GELU, many rows per
+    # expert, dropped picks)
+    small("fp8d_ep_share", 64, 256, 256, 8, 128, w_dtype=FP8_E4M3, gate=SIGMOID,
+          e_end=32, remote=True, fp8d=True, seed_off=60),
+    small("fp8d_gelu", 80, 256, 8, 2, 256, w_dtype=FP8_E4M3, act=GELU, fp8d=True,
+          seed_off=61),
+    small("fp8d_many_rows", 400, 512, 8, 2, 256, w_dtype=FP8_E4M3, fp8d=True,
+          seed_off=62),
+    small("fp8d_threshold", 64, 256, 256, 8, 128, w_dtype=FP8_E4M3, gate=SIGMOID,
+          e_end=32, remote=True, min_prob=0.89, fp8d=True, seed_off=56),
 ]
 
 
@@ -176,3 +187,26 @@ def test_ksplit_matches_unsplit():
     say(f"  split vs unsplit y_perm rel-L2 {e:.3e}")
     assert e <= 1e-3
     full_parity(cfg, inp, a)
+
+
+def test_fp8_dispatch_accuracy_against_the_16bit_transport():
+    """The fp8 transport changes the layer's output by the rounding of E4M3
+    activations: the GPU's change (fp8 vs bf16 rows) matches the oracle's
+    change on the same inputs, and stays a few percent."""
+    cfg16 = small("fp8w_bf16_rows", 96, 512, 8, 2, 256, w_dtype=FP8_E4M3, seed_off=63)
+    cfg8 = cfg16.with_(name="fp8w_fp8_rows", fp8_dispatch=True)
+    inp = make_inputs(cfg16, "cpu")
+    dev = to_device(inp)
+    a = gpu_layer(cfg16, dev)
+    b = gpu_layer(cfg8, dev)
+    gpu_delta = rel_l2(O.decode(stored(b.out), "bf16"), O.decode(stored(a.out), "bf16"))
+    st = np_stored(inp)
+    logits = a.logits.cpu().numpy()
+    ref16 = O.layer_forward(params(cfg16), st["x"], st["w_router"], st["bias"], st["w13"],
+                            st["w2"], st["w13_scale"], st["w2_scale"], logits=logits)
+    ref8 = O.layer_forward(params(cfg8), st["x"], st["w_router"], st["bias"], st["w13"],
+                           st["w2"], st["w13_scale"], st["w2_scale"], logits=logits)
+    ora_delta = rel_l2(ref8["out"], ref16["out"])
+    say(f"  fp8 vs bf16 transport: out rel-L2 GPU {gpu_delta:.4f}, oracle {ora_delta:.4f}")
+    assert 0.005 < ora_delta < 0.08
+    assert abs(gpu_delta - ora_delta) <= 0.2 * ora_delta

@@ -359,6 +359,68 @@ def test_dispatch_and_combine_with_dropped_picks():
             assert out[t, c] == np.float32(acc)
 
 
+# fp8 transport of the dispatched rows (ThunderEP page, section 3.3)
+
+
+def test_e4m3_encode_round_trips_every_finite_code():
+    codes = np.arange(256, dtype=np.uint8)
+    fin = codes[~np.isnan(O.e4m3_decode(codes))]
+    assert len(fin) == 254
+    assert np.array_equal(O.e4m3_encode(O.e4m3_decode(fin)), fin)
+
+
+def test_e4m3_encode_ties_to_even_and_matches_torch():
+    """Every midpoint between adjacent finite magnitudes goes to the code with
+    an even mantissa; random values agree with torch's float8_e4m3fn cast."""
+    pos = np.arange(0, 0x7F, dtype=np.uint8)          # 0 .. 448 ascending
+    v = O.e4m3_decode(pos)
+    mid = (v[:-1] + v[1:]) / 2
+    got = O.e4m3_encode(mid)
+    want = np.where(pos[:-1] % 2 == 0, pos[:-1], pos[1:])
+    assert np.array_equal(got, want)
+    assert np.array_equal(O.e4m3_encode(-mid), want | 0x80)
+    x = np.concatenate([mid, rng.uniform(-448, 448, 20000), rng.normal(size=20000) * 1e-2])
+    t = torch.tensor(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(x), t)
+
+
+def test_e4m3_encode_saturates_and_keeps_sign():
+    got = O.e4m3_encode([464.0, 470.0, 1e9, -1e9, 0.0, -0.0, -1e-9, 2.0 ** -10,
+                         3 * 2.0 ** -10, float("nan")])
+    assert got.tolist() == [0x7E, 0x7E, 0x7E, 0xFE, 0x00, 0x80, 0x80, 0x00, 0x02, 0x7F]
+
+
+def test_row_exponent_closed_form():
+    amax = [448.0, np.nextafter(448.0, 1e9), 224.0, np.nextafter(224.0, 1e9), 1.0,
+            0.0, 2.0 ** -133, 3.0e38]
+    got = O.e4m3_row_exponent(amax).tolist()
+    assert got == [0, 1, -1, 0, -8, 0, -141, 120]
+    for a, e in zip(amax[:5] + amax[6:], got[:5] + got[6:]):
+        assert a <= 448.0 * 2.0 ** e and a > 448.0 * 2.0 ** (e - 1)
+
+
+def test_row_quantisation_scales_and_codes():
+    """Per-row power-of-two scales put each row's amax in (224, 448]; the codes
+    are the library's float8_e4m3fn cast of the exactly scaled row."""
+    r = np.random.default_rng(81)
+    mags = 10.0 ** r.uniform(-30, 30, size=64)
+    x = O.bf16_decode(O.bf16_encode(r.normal(size=(64, 96)) * mags[:, None]))
+    x[5] = 0.0
+    codes, sc = O.quantize_rows_e4m3(x)
+    e = np.log2(sc.astype(np.float64))
+    assert np.all(e == np.round(e))                       # powers of two
+    amax = np.abs(x).max(axis=1)
+    ratio = amax[amax > 0] / sc[amax > 0]
+    assert np.all((ratio > 224) & (ratio <= 448))
+    assert sc[5] == 1.0 and np.all(codes[5] == 0)
+    t = torch.tensor(np.ldexp(x, -e.astype(np.int64)[:, None])).to(torch.float8_e4m3fn)
+    assert np.array_equal(codes, t.view(torch.uint8).numpy())
+    deq = O.e4m3_decode(codes) * sc.astype(np.float64)[:, None]
+    # half a step of 3 mantissa bits, or half the subnormal quantum 2^-9 * scale
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * sc.astype(np.float64)[:, None])
+    assert np.all(np.abs(deq - x) <= bound)
+
+
 # ---------------------------------------------------------------------------
 # Dispatch
 # ---------------------------------------------------------------------------
