@@ -14,6 +14,7 @@ oracle timed on a bounded sample of the same workload.
 """
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -63,6 +64,9 @@ def parse():
                     help="softmax temperature of the gate (default: the workload's, 1.0)")
     ap.add_argument("--min-prob", type=float, default=0.0,
                     help="minimum-probability threshold of the gate (0: off)")
+    ap.add_argument("--replicate-hot", type=int, default=0, metavar="R",
+                    help="give the most loaded local expert R extra physical copies "
+                         "(placement hook) and collect per-expert load statistics")
     ap.add_argument("--fp8-dispatch", action="store_true",
                     help="send the dispatched rows as E4M3 codes with a per-row scale "
                          "into an fp8 x fp8 GEMM-1 (fp8-weight workloads)")
@@ -151,10 +155,40 @@ def main():
     if cfg.fp8_dispatch and (cfg.w_dtype != "e4m3" or args.fused):
         sys.exit("--fp8-dispatch needs an fp8-weight workload (c5) and the unfused path")
     lay = MoELayer(spec, dev)
-    if inp["y_remote"] is not None:
-        lay.y_perm.copy_(inp["y_remote"])
     x, wr, bias = inp["x"], inp["w_router"], inp["bias"]
     w13, w2, s13, s2 = inp["w13"], inp["w2"], inp["w13_scale"], inp["w2_scale"]
+    R = args.replicate_hot
+    if R > 0:
+        if args.fused or cfg.w_dtype == "e4m3":
+            sys.exit("--replicate-hot runs the unfused 16-bit-weight path")
+        # the most loaded local expert (from one routing pass, untimed) gets R
+        # copies at physical slots e_end .. e_end+R-1; experts above the local
+        # range move up by R
+        lay.route(x, wr, bias)
+        e0, e1 = cfg.e_begin, cfg.e_end
+        picks = lay.topk_idx.flatten()
+        cnt = torch.bincount(picks[picks >= 0].long(), minlength=cfg.E)
+        hot = e0 + int(cnt[e0:e1].argmax())
+        phys_of = [e if e < e1 else e + R for e in range(cfg.E)]
+        rep_off = [0]
+        rep_phys = []
+        for e in range(cfg.E):
+            rep_phys.append(phys_of[e])
+            if e == hot:
+                rep_phys += list(range(e1, e1 + R))
+            rep_off.append(len(rep_phys))
+        spec = dataclasses.replace(spec, E_phys=cfg.E + R, e_end=e1 + R)
+        del lay
+        lay = MoELayer(spec, dev)
+        lay.set_placement(torch.tensor(rep_off, dtype=torch.int32, device=dev),
+                          torch.tensor(rep_phys, dtype=torch.int32, device=dev))
+        lay.enable_load_stats()
+        loc = torch.arange(e0, e1, device=dev)
+        own = torch.cat([loc - e0, torch.full((R,), hot - e0, device=dev, dtype=loc.dtype)])
+        w13, w2 = w13[own].contiguous(), w2[own].contiguous()
+        gate_tag += f" [expert {hot} replicated {R}x, load statistics on]"
+    if inp["y_remote"] is not None:
+        lay.y_perm.copy_(inp["y_remote"])
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -228,8 +262,8 @@ def main():
 
     # -- algorithmic bytes and flops from this run's counts ---------------
     counts = lay.counts.cpu().numpy().astype(np.int64)
-    idx = lay.topk_idx.cpu().numpy()
-    e0, e1 = cfg.e_begin, cfg.e_end
+    idx = lay.topk_disp.cpu().numpy()      # physical slots when experts are placed
+    e0, e1 = lay.spec.local
     rows_loc = int(counts[e0:e1].sum())
     ab = x.element_size()
     H, I, T, k, E = cfg.H, cfg.I, cfg.T, cfg.k, cfg.E

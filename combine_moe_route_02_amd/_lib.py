@@ -23,7 +23,8 @@ WS_DISPATCH, WS_FFN, WS_FUSED = 0, 1, 2
 
 EXPORTS = ["moe_route", "moe_dispatch", "moe_dispatch_fp8", "moe_expert_ffn",
            "moe_expert_ffn_up", "moe_expert_ffn_up_fp8", "moe_expert_ffn_down",
-           "moe_combine", "moe_layer_fused", "moe_workspace_bytes", "moe_status_string"]
+           "moe_combine", "moe_layer_fused", "moe_place_experts", "moe_expert_load_stats",
+           "moe_workspace_bytes", "moe_status_string"]
 
 
 class MoeError(RuntimeError):
@@ -45,6 +46,8 @@ _SIGS = {
     "moe_expert_ffn_down": [P, I, I, I, I, I, I, P, P, I, P, P, P, SZ, P],
     "moe_combine": [P, P, P, I, I, I, I, P, P],
     "moe_layer_fused": [P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, SZ, P],
+    "moe_place_experts": [P, I, I, I, I, P, P, P, P],
+    "moe_expert_load_stats": [P, I, I, I, P, P],
     "moe_workspace_bytes": [I, I, I, I, I, I],
     "moe_status_string": [I],
 }
@@ -171,6 +174,20 @@ def moe_layer_fused(x, offsets, slot_of, row_token, topk_w, E, I, e_begin, e_end
         DTYPE_OF[x.dtype], T, H, E, k, I, e_begin, e_end, act, ptr(w13), ptr(w2),
         ptr(h_ws), ptr(y_perm), ptr(out), ptr(ws), ws.numel() * ws.element_size(),
         stream_handle(stream)))
+
+
+def moe_place_experts(topk_idx, E_log, E_phys, rep_offsets, rep_phys, topk_phys,
+                      stream=None):
+    T, k = topk_idx.shape
+    check("moe_place_experts", lib().moe_place_experts(
+        ptr(topk_idx), T, k, E_log, E_phys, ptr(rep_offsets), ptr(rep_phys), ptr(topk_phys),
+        stream_handle(stream)))
+
+
+def moe_expert_load_stats(topk_idx, E, stats, stream=None):
+    T, k = topk_idx.shape
+    check("moe_expert_load_stats", lib().moe_expert_load_stats(
+        ptr(topk_idx), T, k, E, ptr(stats), stream_handle(stream)))
 
 
 def moe_workspace_bytes(which, T, H, E, k, I) -> int:

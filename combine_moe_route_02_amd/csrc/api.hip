@@ -14,6 +14,11 @@ int dispatch_impl(const void* x, int act_dtype, const int32_t* idx, int T, int H
                   int32_t* offsets, int32_t* slot_of, int32_t* row_token,
                   void* x_perm, float* x_scale, void* ws, hipStream_t s);
 size_t dispatch_ws_bytes(int T, int E);
+int place_impl(const int32_t* idx, int T, int k, int E_log, int E_phys,
+               const int32_t* rep_offsets, const int32_t* rep_phys, int32_t* phys,
+               hipStream_t s);
+int load_stats_impl(const int32_t* idx, int T, int k, int E, unsigned long long* stats,
+                    hipStream_t s);
 int combine_impl(const void* y_perm, const int32_t* slot_of, const float* w,
                  int act_dtype, int T, int H, int k, void* out, hipStream_t s);
 int fused_impl(const void* x, const int32_t* offsets, const int32_t* slot_of,
@@ -228,6 +233,26 @@ int moe_expert_ffn(const void* x_perm, const int32_t* offsets, int act_dtype, in
   if (st != MOE_OK) return st;
   return moe_expert_ffn_down(offsets, act_dtype, H, I, e_begin, e_end, max_rows, w2,
                              w2_scale, w_dtype, h_ws, y_perm, ws, ws_bytes, stream);
+}
+
+int moe_place_experts(const int32_t* topk_idx, int T, int k, int E_log, int E_phys,
+                      const int32_t* rep_offsets, const int32_t* rep_phys,
+                      int32_t* topk_phys, hipStream_t stream) {
+  if (T < 0 || k < 1 || k > 32 || E_log < 1 || E_phys < 1 || E_phys > 1024)
+    return MOE_ERR_ARG;
+  if (!pairs_fit(T, k)) return MOE_ERR_ARG;
+  if (T == 0) return MOE_OK;
+  if (!topk_idx || !rep_offsets || !rep_phys || !topk_phys) return MOE_ERR_ARG;
+  return place_impl(topk_idx, T, k, E_log, E_phys, rep_offsets, rep_phys, topk_phys, stream);
+}
+
+int moe_expert_load_stats(const int32_t* topk_idx, int T, int k, int E, uint64_t* stats,
+                          hipStream_t stream) {
+  if (T < 0 || k < 1 || k > 32 || E < 1 || E > 1024) return MOE_ERR_ARG;
+  if (!pairs_fit(T, k)) return MOE_ERR_ARG;
+  if (T == 0) return MOE_OK;
+  if (!topk_idx || !stats) return MOE_ERR_ARG;
+  return load_stats_impl(topk_idx, T, k, E, (unsigned long long*)stats, stream);
 }
 
 int moe_combine(const void* y_perm, const int32_t* slot_of, const float* topk_w,

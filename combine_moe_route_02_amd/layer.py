@@ -33,10 +33,17 @@ class LayerSpec:
     inv_temperature: float = 1.0
     min_prob: float = 0.0    # gate threshold; 0 = off
     fp8_dispatch: bool = False   # send dispatched rows as E4M3 codes (fp8 weights)
+    E_phys: int = 0          # > 0: picks go to physical expert copies (set_placement);
+                             # the local range then numbers physical slots
+
+    @property
+    def E_disp(self) -> int:
+        """Experts as dispatch, the FFN and combine see them."""
+        return self.E_phys if self.E_phys > 0 else self.E
 
     @property
     def local(self):
-        return self.e_begin, (self.E if self.e_end < 0 else self.e_end)
+        return self.e_begin, (self.E_disp if self.e_end < 0 else self.e_end)
 
     @property
     def max_rows(self) -> int:
@@ -55,8 +62,13 @@ class MoELayer:
         self.logits = torch.empty((s.T, s.E), dtype=torch.float32, device=dev)
         self.topk_idx = torch.empty((s.T, s.k), **i32)
         self.topk_w = torch.empty((s.T, s.k), dtype=torch.float32, device=dev)
-        self.counts = torch.empty((s.E,), **i32)
-        self.offsets = torch.empty((s.E + 1,), **i32)
+        self.counts = torch.empty((s.E_disp,), **i32)
+        self.offsets = torch.empty((s.E_disp + 1,), **i32)
+        # placement: physical expert of every pick, and its information
+        self.topk_phys = torch.empty((s.T, s.k), **i32) if s.E_phys > 0 else None
+        self.topk_disp = self.topk_phys if s.E_phys > 0 else self.topk_idx
+        self.rep_offsets = self.rep_phys = None
+        self.load_stats = None
         self.slot_of = torch.empty((s.T, s.k), **i32)
         self.row_token = torch.empty((N,), **i32)
         # fp8 transport: E4M3 codes and one scale per row instead of x_perm
@@ -69,21 +81,44 @@ class MoELayer:
         self.h = torch.empty((max(s.max_rows, 1), s.I), dtype=s.act_dtype, device=dev)
         self.y_perm = torch.zeros((N, s.H), dtype=s.act_dtype, device=dev)
         self.out = torch.empty((s.T, s.H), dtype=s.act_dtype, device=dev)
-        nb = L.moe_workspace_bytes(L.WS_DISPATCH, s.T, s.H, s.E, s.k, s.I)
+        nb = L.moe_workspace_bytes(L.WS_DISPATCH, s.T, s.H, s.E_disp, s.k, s.I)
         self.ws = torch.empty((max(nb, 16),), dtype=torch.uint8, device=dev)
         self.ws_fused = None
         # FFN workspace: lets the GEMMs split a sparse last round of tiles over K
         self.ws_ffn = None
         if ffn_split:
-            nf = L.moe_workspace_bytes(L.WS_FFN, s.T, s.H, s.E, s.k, s.I)
+            nf = L.moe_workspace_bytes(L.WS_FFN, s.T, s.H, s.E_disp, s.k, s.I)
             self.ws_ffn = torch.empty((nf,), dtype=torch.uint8, device=dev)
 
     # -- the four calls -----------------------------------------------------
+    # -- placement hooks ------------------------------------------------------
+    def set_placement(self, rep_offsets, rep_phys):
+        """Copies of logical expert e: physical slots
+        rep_phys[rep_offsets[e]:rep_offsets[e+1]] (int32 device tensors)."""
+        assert self.spec.E_phys > 0, "the spec has no physical expert slots"
+        self.rep_offsets, self.rep_phys = rep_offsets, rep_phys
+
+    def enable_load_stats(self):
+        """Accumulate picks per logical expert over route calls (int64 view of
+        the uint64 counters; zero it to start a new window)."""
+        self.load_stats = torch.zeros((self.spec.E,), dtype=torch.int64,
+                                      device=self.out.device)
+
+    def _after_route(self, stream):
+        s = self.spec
+        if self.load_stats is not None:
+            L.moe_expert_load_stats(self.topk_idx, s.E, self.load_stats, stream=stream)
+        if s.E_phys > 0:
+            assert self.rep_offsets is not None, "set_placement() first"
+            L.moe_place_experts(self.topk_idx, s.E, s.E_phys, self.rep_offsets,
+                                self.rep_phys, self.topk_phys, stream=stream)
+
     def route(self, x, w_router, bias=None, stream=None):
         s = self.spec
         L.moe_route(x, w_router, bias, s.k, GATES[s.gate], s.renorm, s.inv_temperature,
                     self.logits, self.topk_idx, self.topk_w, stream=stream,
                     min_prob=s.min_prob)
+        self._after_route(stream)
 
     def route_from_logits(self, bias=None, stream=None):
         """Top-k gating on the scores already in self.logits."""
@@ -91,16 +126,17 @@ class MoELayer:
         L.moe_route(None, None, bias, s.k, GATES[s.gate], s.renorm, s.inv_temperature,
                     self.logits, self.topk_idx, self.topk_w,
                     act_dtype=L.DTYPE_OF[s.act_dtype], stream=stream, min_prob=s.min_prob)
+        self._after_route(stream)
 
     def dispatch(self, x, stream=None):
         s = self.spec
         e0, e1 = s.local
         if s.fp8_dispatch:
-            L.moe_dispatch_fp8(x, self.topk_idx, s.E, e0, e1, self.counts, self.offsets,
+            L.moe_dispatch_fp8(x, self.topk_disp, s.E_disp, e0, e1, self.counts, self.offsets,
                                self.slot_of, self.row_token, self.x_q, self.x_scale,
                                self.ws, stream=stream)
             return
-        L.moe_dispatch(x, self.topk_idx, s.E, e0, e1, self.counts, self.offsets,
+        L.moe_dispatch(x, self.topk_disp, s.E_disp, e0, e1, self.counts, self.offsets,
                        self.slot_of, self.row_token, self.x_perm, self.ws, stream=stream)
 
     def ffn_up(self, w13, w13_scale=None, stream=None):
@@ -149,18 +185,18 @@ class MoELayer:
         s = self.spec
         e0, e1 = s.local
         if self.ws_fused is None:
-            nb = L.moe_workspace_bytes(L.WS_FUSED, s.T, s.H, s.E, s.k, s.I)
+            nb = L.moe_workspace_bytes(L.WS_FUSED, s.T, s.H, s.E_disp, s.k, s.I)
             self.ws_fused = torch.empty((max(nb, 16),), dtype=torch.uint8,
                                         device=self.out.device)
         L.moe_layer_fused(x, self.offsets, self.slot_of, self.row_token, self.topk_w,
-                          s.E, s.I, e0, e1, ACTS[s.act], w13, w2, self.h, self.y_perm,
+                          s.E_disp, s.I, e0, e1, ACTS[s.act], w13, w2, self.h, self.y_perm,
                           self.out, self.ws_fused, stream=stream)
 
     def dispatch_layout(self, x, stream=None):
         """Counts, offsets and the layout map only (no permuted copy of x):
         the fused kernel reads token rows through the layout map."""
         s = self.spec
-        L.moe_dispatch(x, self.topk_idx, s.E, 0, 0, self.counts, self.offsets,
+        L.moe_dispatch(x, self.topk_disp, s.E_disp, 0, 0, self.counts, self.offsets,
                        self.slot_of, self.row_token, self.x_perm, self.ws, stream=stream)
 
     def forward_fused(self, x, w_router, bias, w13, w2, stream=None) -> torch.Tensor:

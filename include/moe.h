@@ -8,7 +8,9 @@
  *   moe_expert_ffn grouped expert FFN (GEMM-1 + activation, GEMM-2)
  *   moe_combine    gate-weighted sum of each token's k expert outputs
  * plus moe_layer_fused, which runs gather -> GEMM-1 -> GEMM-2 -> combine as
- * one persistent, token-tile-pipelined kernel.
+ * one persistent, token-tile-pipelined kernel; the fp8 transport pair
+ * moe_dispatch_fp8 / moe_expert_ffn_up_fp8; and the placement hooks
+ * moe_place_experts (replicated experts) and moe_expert_load_stats.
  *
  * Conventions (all calls):
  *  - Every pointer is a device pointer unless stated otherwise; the caller
@@ -274,6 +276,48 @@ int moe_layer_fused(const void* x, const int32_t* offsets,
                     int k, int I, int e_begin, int e_end, int act,
                     const void* w13, const void* w2, void* h_ws, void* y_perm,
                     void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_place_experts - logical -> physical expert of every pick.
+ *
+ * Defines: the routing component of large-scale EP reads the placement
+ * information so that hot experts can be replicated and their copies placed
+ * on physical expert slots (TensorRT-LLM large-EP page, high-level design:
+ * GPU-side routing and MoE components adjusted for dynamic placement).
+ *
+ *  topk_idx     [T][k] int32 logical experts (moe_route), -1 = dropped.
+ *  rep_offsets  [E_log+1] int32: the copies of logical expert e are entries
+ *               [rep_offsets[e], rep_offsets[e+1]) of rep_phys (at least one).
+ *  rep_phys     int32 physical slot of each copy, in [0, E_phys).
+ *  topk_phys    [T][k] int32 output: pick j of token t goes to copy
+ *               t mod n_e of its expert (n_e copies): an expert's tokens
+ *               take its copies in turn.  Dropped picks stay -1, and so
+ *               does a pick whose copy names a slot outside [0, E_phys).
+ *               rep_offsets must be nondecreasing and index inside
+ *               rep_phys (not checked: device data is never read on the
+ *               host).
+ * moe_dispatch, moe_expert_ffn and moe_combine then run on topk_phys with
+ * E = E_phys, the weights of every physical slot in place (a copy holds its
+ * logical expert's weights).  topk_w is unchanged.
+ */
+int moe_place_experts(const int32_t* topk_idx, int T, int k, int E_log, int E_phys,
+                      const int32_t* rep_offsets, const int32_t* rep_phys,
+                      int32_t* topk_phys, hipStream_t stream);
+
+/*
+ * moe_expert_load_stats - online per-expert load statistics.
+ *
+ * Defines: the statistics component that counts the traffic of every
+ * expert on the GPU, the input of the replication and placement computation
+ * (TensorRT-LLM large-EP page, high-level design, GPU side).
+ *
+ *  topk_idx  [T][k] int32 (-1 = dropped, not counted).
+ *  stats     [E] uint64, accumulated: stats[e] += number of picks of e in
+ *            this call.  The caller zeroes it when a statistics window
+ *            starts; calls on one stream accumulate in order.
+ */
+int moe_expert_load_stats(const int32_t* topk_idx, int T, int k, int E,
+                          uint64_t* stats, hipStream_t stream);
 
 /* Workspace bytes needed by moe_dispatch (MOE_WS_DISPATCH), moe_expert_ffn
  * and its halves (MOE_WS_FFN: one 256 KB partial-sum slot per compute unit

@@ -377,6 +377,38 @@ def gather_rows(x_stored: np.ndarray, row_token: np.ndarray, r_begin: int,
     return x_stored[row_token[r_begin:r_end]]
 
 
+def place_experts(idx: np.ndarray, rep_offsets: np.ndarray,
+                  rep_phys: np.ndarray) -> np.ndarray:
+    """Physical expert of every pick (TensorRT-LLM large-EP page, high-level
+    design: routing reads the placement information of replicated experts).
+
+    Logical expert e has copies rep_phys[rep_offsets[e]:rep_offsets[e+1]];
+    pick j of token t goes to copy number t mod (number of copies).  Dropped
+    picks (-1) stay -1.
+    """
+    T, k = idx.shape
+    out = np.full((T, k), -1, dtype=np.int32)
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            if e < 0:
+                continue
+            b = int(rep_offsets[e])
+            n = int(rep_offsets[e + 1]) - b
+            out[t, j] = rep_phys[b + t % n]
+    return out
+
+
+def expert_load(idx: np.ndarray, E: int) -> np.ndarray:
+    """Online load statistics: picks per logical expert (dropped picks not
+    counted), as uint64 (the same page's GPU-side statistics component)."""
+    load = np.zeros(E, dtype=np.uint64)
+    for e in idx.reshape(-1):
+        if e >= 0:
+            load[e] += np.uint64(1)
+    return load
+
+
 # ---------------------------------------------------------------------------
 # 4. Expert FFN
 # ---------------------------------------------------------------------------
@@ -474,7 +506,8 @@ def layer_forward(p: LayerParams, x_stored: np.ndarray,
                   w2_stored: np.ndarray, w13_scale: Optional[np.ndarray] = None,
                   w2_scale: Optional[np.ndarray] = None,
                   y_remote_stored: Optional[np.ndarray] = None,
-                  logits: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                  logits: Optional[np.ndarray] = None,
+                  placement=None) -> Dict[str, np.ndarray]:
     """The full layer on stored inputs (bit patterns / float32 values).
 
     ``logits`` may be given (float32) instead of being computed from the
@@ -482,12 +515,21 @@ def layer_forward(p: LayerParams, x_stored: np.ndarray,
     scores another implementation produced.  Rows of experts outside
     [e_begin, e_end) are taken from ``y_remote_stored`` (outputs received
     from other GPUs); local rows are this expert FFN's results.
+
+    ``placement`` = (rep_offsets, rep_phys, E_phys) replaces every logical
+    pick by its physical copy (place_experts) before dispatch; the expert
+    range and the weights are then those of the physical slots.
     """
     x64 = decode(x_stored, p.act_dtype)
     if logits is None:
         logits = router_logits(x64, decode(w_router_stored, p.act_dtype))
     idx, w = route(logits, bias, p.k, p.gate, p.renorm, p.inv_temperature, p.min_prob)
-    counts = expert_counts(idx, p.E)
+    E = p.E
+    idx_log = idx
+    if placement is not None:
+        rep_offsets, rep_phys, E = placement
+        idx = place_experts(idx, rep_offsets, rep_phys)
+    counts = expert_counts(idx, E)
     offsets = expert_offsets(counts)
     slot_of, row_token = layout_map(idx, offsets)
     r0, r1 = int(offsets[p.e_begin]), int(offsets[p.e_end])
@@ -513,7 +555,7 @@ def layer_forward(p: LayerParams, x_stored: np.ndarray,
         w13, w2 = expert_weights(p, w13_stored, w2_stored, w13_scale, w2_scale, el)
         y_perm[r0 + a:r0 + b] = expert_ffn(xp64[a:b], w13, w2, p.act, p.act_dtype)
     out = combine(y_perm, slot_of, w, p.act_dtype)
-    return dict(logits=logits, topk_idx=idx, topk_w=w, counts=counts,
+    return dict(logits=logits, topk_idx=idx_log, topk_phys=idx, topk_w=w, counts=counts,
                 offsets=offsets, slot_of=slot_of, row_token=row_token,
                 x_perm=x_perm, x_scale=x_scale, y_perm=y_perm, out=out)
 

@@ -154,6 +154,20 @@ def test_fp8_transport_validation():
     assert u(FAKE, FAKE, FAKE, 256, 128, 3, 3, 64, 0, FAKE, FAKE, FAKE, None) == L.MOE_OK
 
 
+def test_placement_and_stats_validation():
+    lib = L.lib()
+    pl = lib.moe_place_experts
+    assert pl(FAKE, 4, 2, 8, 0, FAKE, FAKE, FAKE, None) == L.MOE_ERR_ARG    # E_phys
+    assert pl(FAKE, 4, 2, 8, 2000, FAKE, FAKE, FAKE, None) == L.MOE_ERR_ARG
+    assert pl(FAKE, 4, 0, 8, 8, FAKE, FAKE, FAKE, None) == L.MOE_ERR_ARG     # k
+    assert pl(FAKE, 4, 2, 8, 8, None, FAKE, FAKE, None) == L.MOE_ERR_ARG
+    assert pl(FAKE, 0, 2, 8, 8, None, None, None, None) == L.MOE_OK         # nothing to do
+    st = lib.moe_expert_load_stats
+    assert st(FAKE, 4, 2, 0, FAKE, None) == L.MOE_ERR_ARG
+    assert st(FAKE, 4, 2, 8, None, None) == L.MOE_ERR_ARG
+    assert st(None, 0, 2, 8, None, None) == L.MOE_OK
+
+
 def test_combine_and_fused_validation():
     lib = L.lib()
     assert lib.moe_combine(FAKE, FAKE, FAKE, L.DTYPE_BF16, 4, 64, 0, FAKE, None) == L.MOE_ERR_ARG

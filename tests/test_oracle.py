@@ -539,6 +539,79 @@ def test_fp8_block_dequant_uses_row_block_then_column_block():
 
 
 # ---------------------------------------------------------------------------
+# Placement of replicated experts and load statistics (TensorRT-LLM
+# large-EP page, high-level design)
+# ---------------------------------------------------------------------------
+
+
+def test_identity_placement_is_the_identity():
+    idx = _random_routing(50, 8, 3, 4)
+    idx[::7, 2] = -1
+    out = O.place_experts(idx, np.arange(9), np.arange(8))
+    assert np.array_equal(out, idx)
+
+
+def test_placement_spreads_an_expert_over_its_copies_in_token_order():
+    """Every token picks expert 0, which has n copies: copy r serves tokens
+    r, r + n, ... (ceil((T - r) / n) of them); other experts keep one copy."""
+    T, n = 103, 4
+    idx = np.zeros((T, 1), np.int32)
+    rep_off = np.array([0, n, n + 1])
+    rep_phys = np.array([5, 0, 2, 7, 1])
+    out = O.place_experts(idx, rep_off, rep_phys)
+    for r, p in enumerate(rep_phys[:n]):
+        assert np.array_equal(np.nonzero(out[:, 0] == p)[0], np.arange(r, T, n))
+        assert (out == p).sum() == -(-(T - r) // n)
+
+
+def test_placement_conserves_every_logical_load():
+    r = np.random.default_rng(82)
+    T, E, k = 400, 16, 4
+    idx = _random_routing(T, E, k, 11)
+    idx[r.random((T, k)) < 0.1] = -1
+    ncopy = r.integers(1, 4, size=E)
+    rep_off = np.concatenate([[0], np.cumsum(ncopy)])
+    rep_phys = r.permutation(int(ncopy.sum())).astype(np.int32)
+    phys = O.place_experts(idx, rep_off, rep_phys)
+    assert np.array_equal(phys < 0, idx < 0)
+    pload = O.expert_counts(phys, int(ncopy.sum()))
+    lload = O.expert_load(idx, E)
+    assert np.array_equal(lload, np.bincount(idx[idx >= 0], minlength=E).astype(np.uint64))
+    for e in range(E):
+        assert pload[rep_phys[rep_off[e]:rep_off[e + 1]]].sum() == lload[e]
+    for t in range(0, T, 13):                  # brute force, one pick at a time
+        for j in range(k):
+            e = idx[t, j]
+            if e >= 0:
+                assert phys[t, j] == rep_phys[rep_off[e] + t % ncopy[e]]
+
+
+def test_replicated_layer_equals_the_unreplicated_layer():
+    """Copies hold their expert's weights, so routing picks to copies changes
+    no output (the float64 sums are the same numbers in the same order)."""
+    r = np.random.default_rng(83)
+    p = O.LayerParams(T=40, H=16, E=4, k=2, I=8, act_dtype=O.F32, w_dtype=O.F32,
+                      gate="softmax", renorm=False, act="swiglu", e_begin=0, e_end=4)
+    x = r.normal(size=(40, 16)).astype(np.float32)
+    wr = (r.normal(size=(4, 16)) / 4).astype(np.float32)
+    w13 = (r.normal(size=(4, 16, 16)) / 4).astype(np.float32)
+    w2 = (r.normal(size=(4, 16, 8)) / 3).astype(np.float32)
+    base = O.layer_forward(p, x, wr, None, w13, w2)
+    ncopy = np.array([1, 3, 1, 2])
+    rep_off = np.concatenate([[0], np.cumsum(ncopy)])
+    rep_phys = np.array([0, 1, 4, 5, 2, 3, 6], np.int32)
+    owner = np.empty(7, np.int64)
+    for e in range(4):
+        owner[rep_phys[rep_off[e]:rep_off[e + 1]]] = e
+    pp = O.LayerParams(**{**p.__dict__, "e_end": 7})
+    rep = O.layer_forward(pp, x, wr, None, w13[owner], w2[owner],
+                          placement=(rep_off, rep_phys, 7))
+    assert np.array_equal(rep["out"], base["out"])
+    assert np.array_equal(rep["topk_idx"], base["topk_idx"])
+    assert sorted(np.unique(rep["topk_phys"]).tolist()) == list(range(7))
+
+
+# ---------------------------------------------------------------------------
 # Combine and the whole layer
 # ---------------------------------------------------------------------------
 
