@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--replicate-hot", type=int, default=0, metavar="R",
                     help="give the most loaded local expert R extra physical copies "
                          "(placement hook) and collect per-expert load statistics")
+    ap.add_argument("--microbatch", type=int, default=0, metavar="N",
+                    help="run the layer as N token chunks on two streams (data movement "
+                         "of one chunk overlapping another's expert GEMMs)")
     ap.add_argument("--fp8-dispatch", action="store_true",
                     help="send the dispatched rows as E4M3 codes with a per-row scale "
                          "into an fp8 x fp8 GEMM-1 (fp8-weight workloads)")
@@ -190,8 +193,24 @@ def main():
     if inp["y_remote"] is not None:
         lay.y_perm.copy_(inp["y_remote"])
     stream = torch.cuda.current_stream()
+    NB = args.microbatch
+    if NB > 1:
+        if args.fused or R > 0:
+            sys.exit("--microbatch runs the unfused layer without placement")
+        from combine_moe_route_02_amd import MicrobatchedLayer
+        mb = MicrobatchedLayer(spec, NB, dev)
+        if inp["y_remote"] is not None:     # received rows: each chunk's own slice
+            for c in mb.layers:
+                c.y_perm.copy_(inp["y_remote"][: c.y_perm.shape[0]])
+        gate_tag += f" [{NB} micro-batches on two streams]"
+        up_ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(NB)] for _ in range(args.steps)]
 
-    def step(ev=None):
+    def step(ev=None, i=None):
+        if NB > 1:
+            mb.forward(x, wr, bias, w13, w2, s13, s2,
+                       up_events=up_ev[i] if i is not None else None)
+            return
         lay.route(x, wr, bias)
         if args.fused:
             lay.dispatch_layout(x)
@@ -234,12 +253,15 @@ def main():
     wall0 = time.perf_counter()
     t0.record(stream)
     for i in range(K):
-        step(kev[i])
+        step(kev[i], i)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = t0.elapsed_time(t1) / K
-    gemm1_ms = float(np.mean([a.elapsed_time(b) for a, b in kev]))
+    if NB > 1:   # GEMM-1 launches of every chunk, on the compute stream
+        gemm1_ms = float(np.mean([a.elapsed_time(b) for st in up_ev for a, b in st]))
+    else:
+        gemm1_ms = float(np.mean([a.elapsed_time(b) for a, b in kev]))
     print(f"[bench] {K} steps: {ms_per_step:.4f} ms/step (wall {wall:.3f} s)",
           file=sys.stderr, flush=True)
 
@@ -285,8 +307,13 @@ def main():
     gemm_tflops = (flops1 + flops2) / ((stage_ms["ffn_up"] + stage_ms["ffn_down"]) * 1e9)
     if args.fused:
         flops1 += flops2   # the fused kernel runs both GEMMs (and combine)
+    if NB > 1:
+        flops1 /= NB       # one GEMM-1 launch per micro-batch (average share)
+        wb1_share = 1.0 / NB
+    else:
+        wb1_share = 1.0
     if cfg.w_dtype == "e4m3":
-        bytes1 = wb1 + rows_loc * row_out + rows_loc * I * ab
+        bytes1 = wb1 + (rows_loc * row_out + rows_loc * I * ab) * wb1_share
         achieved = bytes1 / (gemm1_ms * 1e6)
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4)}
@@ -306,6 +333,8 @@ def main():
             " (GEMM-1 + SwiGLU, fp8 weights, moe_expert_ffn_up)"
     else:
         kname = "grouped_gemm_dma (GEMM-1 + SwiGLU, moe_expert_ffn_up)"
+    if NB > 1:
+        kname += f", one launch per micro-batch of {T // NB} tokens"
     roof["kernel"] = kname
     roof["avg_launch_ms"] = round(gemm1_ms, 5)
     # counters were taken on the workload's own gating only

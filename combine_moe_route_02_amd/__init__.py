@@ -8,4 +8,4 @@ from ._lib import (MoeError, lib, moe_combine, moe_dispatch, moe_dispatch_fp8,  
                    moe_expert_ffn, moe_expert_ffn_down, moe_expert_ffn_up,
                    moe_expert_ffn_up_fp8, moe_expert_load_stats, moe_layer_fused,
                    moe_place_experts, moe_route, moe_workspace_bytes)
-from .layer import LayerSpec, MoELayer  # noqa: F401
+from .layer import LayerSpec, MicrobatchedLayer, MoELayer  # noqa: F401

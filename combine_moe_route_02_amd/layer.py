@@ -6,6 +6,7 @@ kernel after route and dispatch.  Nothing here computes any part of the
 layer.
 """
 
+import dataclasses
 from dataclasses import dataclass
 from typing import Optional
 
@@ -203,4 +204,86 @@ class MoELayer:
         self.route(x, w_router, bias, stream)
         self.dispatch_layout(x, stream)
         self.fused(x, w13, w2, stream)
+        return self.out
+
+
+class MicrobatchedLayer:
+    """The layer over token chunks on two streams (ThunderEP page, section
+    3.2: micro-batches whose data movement overlaps the previous micro-batch's
+    expert GEMMs; 4-8 chunks suggested).
+
+    Each chunk is a MoELayer of its own tokens (routing is per token, so
+    the chunks route exactly as the whole batch would); their outputs are
+    row slices of one output tensor.  Route, dispatch and combine of every
+    chunk run on the memory stream, the expert FFN on the compute stream.
+    Chunk i's FFN waits for its dispatch, its combine for its FFN, and the
+    memory stream takes chunk i+1's route and dispatch before chunk i's
+    combine, so data movement of one chunk overlaps another chunk's GEMMs.
+    Streams keep the default priority.  The FFN calls are serialised on the
+    compute stream, so the chunks share one FFN workspace.
+    """
+
+    def __init__(self, spec: LayerSpec, n_chunks: int, device="cuda", ffn_split=True):
+        assert 1 <= n_chunks <= max(spec.T, 1)
+        dev = torch.device(device)
+        self.spec = spec
+        self.bounds = [spec.T * i // n_chunks for i in range(n_chunks + 1)]
+        self.out = torch.empty((spec.T, spec.H), dtype=spec.act_dtype, device=dev)
+        self.layers = []
+        for i in range(n_chunks):
+            lay = MoELayer(dataclasses.replace(spec, T=self.bounds[i + 1] - self.bounds[i]),
+                           dev, ffn_split=False)
+            lay.out = self.out[self.bounds[i]:self.bounds[i + 1]]
+            self.layers.append(lay)
+        if ffn_split:
+            nf = L.moe_workspace_bytes(L.WS_FFN, spec.T, spec.H, spec.E_disp, spec.k, spec.I)
+            ws = torch.empty((nf,), dtype=torch.uint8, device=dev)
+            for lay in self.layers:
+                lay.ws_ffn = ws
+        self.s_mem = torch.cuda.Stream(dev)
+        self.s_comp = torch.cuda.Stream(dev)
+        self.ev_disp = [torch.cuda.Event() for _ in range(n_chunks)]
+        self.ev_ffn = [torch.cuda.Event() for _ in range(n_chunks)]
+
+    def forward(self, x, w_router, bias, w13, w2, w13_scale=None, w2_scale=None,
+                up_events=None) -> torch.Tensor:
+        """up_events: optional [(start, end)] per chunk, recorded around its
+        GEMM-1 on the compute stream (for timing)."""
+        cur = torch.cuda.current_stream()
+        start = torch.cuda.Event()
+        start.record(cur)
+        self.s_mem.wait_event(start)
+        self.s_comp.wait_event(start)
+        n = len(self.layers)
+
+        def front(i):
+            b0, b1 = self.bounds[i], self.bounds[i + 1]
+            lay = self.layers[i]
+            lay.route(x[b0:b1], w_router, bias, stream=self.s_mem)
+            lay.dispatch(x[b0:b1], stream=self.s_mem)
+            self.ev_disp[i].record(self.s_mem)
+
+        front(0)
+        for i in range(n):
+            lay = self.layers[i]
+            self.s_comp.wait_event(self.ev_disp[i])
+            if up_events is not None:
+                up_events[i][0].record(self.s_comp)
+            lay.ffn_up(w13, w13_scale, stream=self.s_comp)
+            if up_events is not None:
+                up_events[i][1].record(self.s_comp)
+            lay.ffn_down(w2, w2_scale, stream=self.s_comp)
+            self.ev_ffn[i].record(self.s_comp)
+            if i + 1 < n:
+                front(i + 1)
+            self.s_mem.wait_event(self.ev_ffn[i])
+            lay.combine(stream=self.s_mem)
+        end = torch.cuda.Event()
+        end.record(self.s_mem)
+        cur.wait_event(end)
+        # the caller's stream now follows both streams; keep the inputs alive
+        for t in (x, w_router, bias, w13, w2, w13_scale, w2_scale):
+            if t is not None:
+                t.record_stream(self.s_mem)
+                t.record_stream(self.s_comp)
         return self.out

@@ -1,0 +1,46 @@
+"""Micro-batched layer on two streams: the chunks route and compute each
+token exactly as the whole batch does (no k-split: the same per-row sums),
+so the output equals the one-shot layer's bit for bit, and the oracle's
+within the tolerance."""
+
+import numpy as np
+import pytest
+import torch
+
+from gen.configs import F32, GELU
+from gen.inputs import make_inputs
+from oracle import moe_oracle as O
+from oracle.torch_io import stored
+from tests.harness import gpu_layer, np_stored, params, rel_l2, say, spec, to_device, tol
+from tests.test_gpu_small import small
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    (small("mb_bf16", 700, 256, 8, 2, 128, renorm=True, bias="normal", seed_off=80), 3),
+    (small("mb_f32_gelu", 255, 128, 8, 2, 256, act_dtype=F32, act=GELU, seed_off=81), 4),
+    (small("mb_threshold", 500, 256, 16, 4, 128, inv_t=1 / 0.3, min_prob=0.05,
+           seed_off=52), 5),
+]
+
+
+@pytest.mark.parametrize("cfg,n", CASES, ids=[c.name for c, _ in CASES])
+def test_microbatched_equals_whole_batch(cfg, n):
+    from combine_moe_route_02_amd import MicrobatchedLayer
+    inp = make_inputs(cfg, "cpu")
+    dev = to_device(inp)
+    base = gpu_layer(cfg, dev, split=False)
+    say(f"[gpu] {cfg.name} in {n} micro-batches on two streams")
+    mb = MicrobatchedLayer(spec(cfg), n, "cuda", ffn_split=False)
+    for _ in range(2):          # a second call reuses every buffer
+        mb.forward(dev["x"], dev["w_router"], dev["bias"], dev["w13"], dev["w2"])
+    torch.cuda.synchronize()
+    counts = sum(l.counts.cpu().numpy().astype(np.int64) for l in mb.layers)
+    assert np.array_equal(counts, base.counts.cpu().numpy())
+    assert torch.equal(mb.out, base.out), "micro-batched output differs"
+    st = np_stored(inp)
+    ref = O.layer_forward(params(cfg), st["x"], st["w_router"], st["bias"], st["w13"],
+                          st["w2"], logits=base.logits.cpu().numpy())
+    e = rel_l2(O.decode(stored(mb.out), cfg.act_dtype), ref["out"])
+    say(f"  out rel-L2 {e:.3e}")
+    assert e <= tol(cfg)
