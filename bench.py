@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--microbatch", type=int, default=0, metavar="N",
                     help="run the layer as N token chunks on two streams (data movement "
                          "of one chunk overlapping another's expert GEMMs)")
+    ap.add_argument("--graph", choices=["on", "off"], default="off",
+                    help="time replays of the whole step captured in one hipGraph "
+                         "(per-stage times then come from one graph per stage)")
     ap.add_argument("--fp8-dispatch", action="store_true",
                     help="send the dispatched rows as E4M3 codes with a per-row scale "
                          "into an fp8 x fp8 GEMM-1 (fp8-weight workloads)")
@@ -238,9 +241,29 @@ def main():
         b.copy_(a)      # reads n bytes, writes n bytes
         torch.cuda.synchronize()
         del a, b
+    use_graph = args.graph == "on"
+    if use_graph and (NB > 1 or args.fused):
+        sys.exit("--graph captures the unfused single-stream step")
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
+    graph = None
+    if use_graph:
+        # warm up on a side stream, then capture one whole step; every size
+        # the step needs is read on the device, so replays are complete steps
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for _ in range(max(args.warmup, 1)):
+                step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        graph.replay()
+    else:
+        for _ in range(args.warmup):
+            step()
     torch.cuda.synchronize()
 
     # -- timed region: exactly K steps ------------------------------------
@@ -253,11 +276,22 @@ def main():
     wall0 = time.perf_counter()
     t0.record(stream)
     for i in range(K):
-        step(kev[i], i)
+        if graph is not None:
+            graph.replay()
+        else:
+            step(kev[i], i)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = t0.elapsed_time(t1) / K
+    if graph is not None:
+        # GEMM-1 launches on the same stream, eager, between events (each
+        # launch is long against the host's launch overhead)
+        for a, b in kev:
+            a.record(stream)
+            lay.ffn_up(w13, s13)
+            b.record(stream)
+        torch.cuda.synchronize()
     if NB > 1:   # GEMM-1 launches of every chunk, on the compute stream
         gemm1_ms = float(np.mean([a.elapsed_time(b) for st in up_ev for a, b in st]))
     else:
@@ -271,16 +305,34 @@ def main():
              lambda: lay.ffn_up(w13, s13), lambda: lay.ffn_down(w2, s2),
              lambda: lay.combine()]
     reps = max(3, min(K, 10))
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-          for _ in range(reps)]
-    for r in range(reps):
-        ev[r][0].record(stream)
-        for j, c in enumerate(calls):
-            c()
-            ev[r][j + 1].record(stream)
-    torch.cuda.synchronize()
-    stage_ms = {n: float(np.median([ev[r][j].elapsed_time(ev[r][j + 1])
-                                    for r in range(reps)])) for j, n in enumerate(names)}
+    if graph is not None:
+        # one graph per stage, replayed back to back: the stage's own kernel
+        # time, without the host's launch gaps between short kernels
+        stage_ms = {}
+        for n, c in zip(names, calls):
+            gs = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gs):
+                c()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            gs.replay()
+            a.record(stream)
+            for _ in range(reps):
+                gs.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            stage_ms[n] = a.elapsed_time(b) / reps
+            del gs
+    else:
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+              for _ in range(reps)]
+        for r in range(reps):
+            ev[r][0].record(stream)
+            for j, c in enumerate(calls):
+                c()
+                ev[r][j + 1].record(stream)
+        torch.cuda.synchronize()
+        stage_ms = {n: float(np.median([ev[r][j].elapsed_time(ev[r][j + 1])
+                                        for r in range(reps)])) for j, n in enumerate(names)}
 
     # -- algorithmic bytes and flops from this run's counts ---------------
     counts = lay.counts.cpu().numpy().astype(np.int64)
@@ -356,7 +408,8 @@ def main():
         + ("+e4m3a" if cfg.fp8_dispatch else ""),
         "data": "synthetic (seeded generator; random-init weights)",
         "config": {"workload": f"{cfg.name}: {WORKLOAD[cfg.name]}"
-                   + (" [fused kernel]" if args.fused else "") + gate_tag, "tokens": T,
+                   + (" [fused kernel]" if args.fused else "") + gate_tag
+                   + (" [one hipGraph per step]" if graph is not None else ""), "tokens": T,
                    "hidden": H, "experts": E, "local_experts": e1 - e0, "top_k": k,
                    "ffn_inner": I, "local_rows": rows_loc, "kept_picks": n_kept},
         "roofline": roof,

@@ -109,23 +109,41 @@ __device__ __forceinline__ void load8(const typename Act<DT>::T* p, float* f) {
   }
 }
 
-// Router projection on the vector ALUs: one wave computes TPW tokens x EB
-// experts (expert block blockIdx.y); lanes stride over H in 8-element
-// chunks, two chunks per step whose loads (kept packed until use) are all
-// issued before the FMAs, so each wave keeps 2 * (TPW + EB) 16-byte loads in
-// flight.  Used when the projection is too small or too narrow for matrix
-// tiles (few experts, or a decode batch of few tokens).
+// acc + a.lo * b.lo + a.hi * b.hi for two packed 16-bit values
+// (v_dot2_f32_bf16 / v_dot2_f32_f16).
+template <int DT>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  if constexpr (DT == MOE_DTYPE_BF16)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), acc, false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b),
+                                  acc, false);
+}
+
+// Router projection on the vector ALUs: a block computes TPW tokens x EB
+// experts (token block blockIdx.x, expert block blockIdx.y).  Its four waves
+// split H: wave w takes the 8-element chunks c with (c / 64) % 4 == w, two
+// chunks per step whose loads (kept packed until use) are all issued before
+// the arithmetic, so each wave keeps 2 * (TPW + EB) 16-byte loads in flight
+// and a row is covered in a quarter of the dependent load steps.  16-bit
+// inputs go through packed dot products, two multiply-adds per instruction.  The four partial
+// sums of each dot product are added in wave order through LDS (a fixed
+// order: the result does not depend on timing).  Used when the projection is
+// too small or too narrow for matrix tiles (few experts, or a decode batch).
 template <int DT, int TPW, int EB>
 __global__ void __launch_bounds__(256)
     router_valu_kernel(const void* __restrict__ x, const void* __restrict__ wr, int T,
                        int H, int E, float* __restrict__ logits) {
   typedef typename Act<DT>::T ST;
   constexpr int CPE = DT == MOE_DTYPE_F32 ? 2 : 1;  // 16-byte loads per 8 elements
+  __shared__ float part[4][TPW][EB];
   const int lane = lane_id();
-  const int wave = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
-  const int t0 = wave * TPW;
+  const int wave = (int)threadIdx.x >> 6;
+  const int t0 = (int)blockIdx.x * TPW;
   const int e0 = (int)blockIdx.y * EB;
-  if (t0 >= T) return;
   float acc[TPW][EB];
 #pragma unroll
   for (int a = 0; a < TPW; ++a)
@@ -140,12 +158,12 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
   for (int e = 0; e < EB; ++e) wrow[e] = (const uint4*)(W + (long long)min(e0 + e, E - 1) * H);
   const int nch = H >> 3;
-  for (int c = lane; c < nch; c += 128) {
-    const bool two = c + 64 < nch;
+  for (int c = wave * 64 + lane; c < nch; c += 512) {
+    const bool two = c + 256 < nch;
     uint4 xq[2][TPW][CPE], wq[2][EB][CPE];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int cc = (u == 0 || two) ? c + 64 * u : c;
+      const int cc = (u == 0 || two) ? c + 256 * u : c;
 #pragma unroll
       for (int a = 0; a < TPW; ++a)
 #pragma unroll
@@ -158,17 +176,33 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       if (u == 1 && !two) break;
-      float xf[TPW][8];
+      if constexpr (DT == MOE_DTYPE_F32) {
+        float xf[TPW][8];
 #pragma unroll
-      for (int a = 0; a < TPW; ++a) load8<DT>((const ST*)xq[u][a], xf[a]);
+        for (int a = 0; a < TPW; ++a) load8<DT>((const ST*)xq[u][a], xf[a]);
 #pragma unroll
-      for (int e = 0; e < EB; ++e) {
-        float wf[8];
-        load8<DT>((const ST*)wq[u][e], wf);
+        for (int e = 0; e < EB; ++e) {
+          float wf[8];
+          load8<DT>((const ST*)wq[u][e], wf);
 #pragma unroll
-        for (int a = 0; a < TPW; ++a)
+          for (int a = 0; a < TPW; ++a)
 #pragma unroll
-          for (int q = 0; q < 8; ++q) acc[a][e] = fmaf(xf[a][q], wf[q], acc[a][e]);
+            for (int q = 0; q < 8; ++q) acc[a][e] = fmaf(xf[a][q], wf[q], acc[a][e]);
+        }
+      } else {
+        // 16-bit pairs straight into the packed dot product (two products
+        // and the float32 sum per instruction, no unpacking)
+#pragma unroll
+        for (int e = 0; e < EB; ++e) {
+          const uint32_t wv[4] = {wq[u][e][0].x, wq[u][e][0].y, wq[u][e][0].z, wq[u][e][0].w};
+#pragma unroll
+          for (int a = 0; a < TPW; ++a) {
+            const uint32_t xv[4] = {xq[u][a][0].x, xq[u][a][0].y, xq[u][a][0].z,
+                                    xq[u][a][0].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[a][e] = dot2<DT>(xv[q], wv[q], acc[a][e]);
+          }
+        }
       }
     }
   }
@@ -177,8 +211,15 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
     for (int e = 0; e < EB; ++e) {
       const float v = wave_sum(acc[a][e]);
-      if (lane == 0 && t0 + a < T && e0 + e < E) logits[(long long)(t0 + a) * E + e0 + e] = v;
+      if (lane == 0) part[wave][a][e] = v;
     }
+  }
+  __syncthreads();
+  const int i = (int)threadIdx.x;
+  if (i < TPW * EB) {
+    const int a = i / EB, e = i % EB;
+    const float v = ((part[0][a][e] + part[1][a][e]) + part[2][a][e]) + part[3][a][e];
+    if (t0 + a < T && e0 + e < E) logits[(long long)(t0 + a) * E + e0 + e] = v;
   }
 }
 
@@ -187,13 +228,10 @@ namespace {
 template <int DT>
 int launch_router_valu(const void* x, const void* wr, int T, int H, int E,
                        float* logits, hipStream_t s) {
-  const int waves_per_block = 4;
 #define MOE_ROUTER(TPW, EB)                                                          \
   do {                                                                               \
-    const int waves = (T + (TPW) - 1) / (TPW);                                       \
     hipLaunchKernelGGL((router_valu_kernel<DT, TPW, EB>),                            \
-                       dim3((waves + waves_per_block - 1) / waves_per_block,        \
-                            (E + (EB) - 1) / (EB)),                                  \
+                       dim3((T + (TPW) - 1) / (TPW), (E + (EB) - 1) / (EB)),         \
                        dim3(256), 0, s, x, wr, T, H, E, logits);                     \
   } while (0)
   MOE_ROUTER(4, 8);
