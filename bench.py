@@ -512,6 +512,20 @@ def stats_summary(stats_csv, out_path, workload="c2", extra=""):
     for r in rows:
         lines.append(f"{r.get('Calls', '')}, {r.get('TotalDurationNs', '')}, "
                      f"{r.get('AverageNs', '')}, {r.get('Percentage', '')}, {r[name_k][:140]}")
+    # per-dispatch durations of this library's kernels from the kernel trace
+    # written beside the stats: the median (the first launches of a process
+    # include cold caches and page mapping)
+    trace = stats_csv.replace("kernel_stats", "kernel_trace")
+    if trace != stats_csv and os.path.exists(trace):
+        import statistics
+        per = {}
+        for r in _counter_rows(trace):
+            if r["Kernel_Name"].startswith(("void moe::", "moe::")):
+                per.setdefault(r["Kernel_Name"], []).append(
+                    int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        lines.append("# median ns per dispatch (kernel trace), dispatches, kernel")
+        for k, v in sorted(per.items(), key=lambda kv: -statistics.median(kv[1])):
+            lines.append(f"# {statistics.median(v):.0f}, {len(v)}, {k[:120]}")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines[:30]))
