@@ -95,10 +95,20 @@ def gating_of(args):
     return kw, label
 
 
-def source_hash() -> str:
+# Sources that define each measured kernel: a counter summary is valid for
+# the kernel as long as these files are unchanged.
+KERNEL_SOURCES = {
+    "gemm1": ["gemm.hip", "gemm_tile.h", "moe_internal.h", "moe_common.h"],
+    "fused": ["fused.hip", "gemm_tile.h", "moe_internal.h", "moe_common.h"],
+}
+
+
+def source_hash(kernel_key: str = "") -> str:
+    """Hash of the kernel's defining sources (all of csrc/ without a key)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "combine_moe_route_02_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    names = KERNEL_SOURCES.get(kernel_key) or sorted(os.listdir(csrc))
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -118,7 +128,7 @@ def load_traffic(kernel_key: str, workload: str):
                 continue
             k, v = line.split("=", 1)
             rec[k.strip()] = v.strip()
-    if rec.get("source_hash") != source_hash():
+    if rec.get("source_hash") != source_hash(kernel_key):
         return None
     try:
         return float(rec["hbm_bytes_per_launch"])
@@ -489,7 +499,7 @@ def pmc_summary(fetch_csv, write_csv, out_path, calib_mib, workload, extra=""):
         rec.setdefault("hbm_bytes_per_launch", hbm)
         rec.setdefault("fetch_kib_per_launch", fk)
         rec.setdefault("write_kib_per_launch", wk)
-    lines.append(f"source_hash = {source_hash()}")
+    lines.append(f"source_hash = {source_hash('fused' if extra else 'gemm1')}")
     for key, v in rec.items():
         lines.append(f"{key} = {v:.0f}")
     with open(out_path, "w") as f:

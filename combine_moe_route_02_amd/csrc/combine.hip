@@ -11,7 +11,8 @@
 // weights are wave-uniform (scalar loads); each lane owns 16-byte chunks of
 // the slice, accumulates the k products in float32 in pick order and rounds
 // once.  The k loads of a chunk are independent, so each lane keeps k x 16
-// bytes in flight.  Picks with slot -1 (dropped by the gate threshold) add
+// bytes in flight; they are non-temporal loads, since every expert-output
+// row is read exactly once.  Picks with slot -1 (dropped by the gate threshold) add
 // nothing; a token with no kept pick gets a zero row.
 
 #include "moe_internal.h"
@@ -50,7 +51,9 @@ __global__ void __launch_bounds__(256)
     uint4 q[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
-      if (has[j]) q[j] = y_perm[rows[j] + c];
+      if (has[j])  // each row is read once: stream it past the caches
+        q[j] = __builtin_bit_cast(
+            uint4, __builtin_nontemporal_load((const u32x4*)&y_perm[rows[j] + c]));
     float acc[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] = 0.0f;
