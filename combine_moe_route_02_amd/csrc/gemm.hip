@@ -393,8 +393,10 @@ do {                                                                            
     const uint32_t dst_ = lds0 + ((st) % NS) * STAGE;                              \
     const char* ak_ = a_tile + (st) * A_ROWB;                                      \
     const char* bk_ = b_tile + (st) * B_ROWB;                                      \
-    _Pragma("unroll") for (int j = 0; j < BPW; ++j)                                \
-      dma16(j < JA ? ak_ : bk_, voff[j], dst_ + ldsoff[j]);                        \
+    _Pragma("unroll") for (int j = 0; j < BPW; ++j) {                              \
+      if (j < JA) dma16(ak_, voff[j], dst_ + ldsoff[j]);                           \
+      else dma16_stream(bk_, voff[j], dst_ + ldsoff[j]);                           \
+    }                                                                            \
 } while (0)
 
     lds_barrier();  // every wave is done with the previous tile's stages

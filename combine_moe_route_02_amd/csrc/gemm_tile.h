@@ -221,6 +221,16 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t 
                : "memory");
 }
 
+// dma16 with the non-temporal hint, for data that is read once (a decode
+// batch's fp8 weights: each weight line serves one tile).
+__device__ __forceinline__ void dma16_stream(const char* base, uint32_t voff,
+                                             uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(voff), "s"(base), "s"(lds_base)
+               : "memory");
+}
+
 // L2 prefetch: one dword of each lane's line is copied to a scratch LDS
 // slot that nothing reads (lane l writes lds_base + 4 * l), which brings the
 // lines into L2 ahead of their stage's copy.  Counted by vmcnt like dma16.
