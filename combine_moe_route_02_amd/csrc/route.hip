@@ -131,8 +131,8 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
 // and a row is covered in a quarter of the dependent load steps.  16-bit
 // inputs go through packed dot products, two multiply-adds per instruction.  The four partial
 // sums of each dot product are added in wave order through LDS (a fixed
-// order: the result does not depend on timing).  Used when the projection is
-// too small or too narrow for matrix tiles (few experts, or a decode batch).
+// order: the result does not depend on timing).  Used for float32
+// activations and for 16-bit rows whose length is not a multiple of 32.
 template <int DT, int TPW, int EB>
 __global__ void __launch_bounds__(256)
     router_valu_kernel(const void* __restrict__ x, const void* __restrict__ wr, int T,
@@ -223,6 +223,102 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// Router projection on the matrix cores for batches the staged GEMM tiles
+// do not fit (few experts, or a decode batch): one block computes a tile of
+// 16 tokens x 16 experts with v_mfma_f32_16x16x32_{bf16,f16}.  Each lane
+// loads its operands straight from memory, 16 bytes per load: lane l reads
+// row l % 16 (a token of x, an expert of Wr) at the 8-element chunk l / 16
+// of every 32-wide k step, so each activation is read once per expert tile
+// and one tile covers all experts when there are at most 16.  The NW waves
+// of the block take consecutive ranges of k steps, keep two batches of U k
+// steps of loads in flight, and their partial 16x16 sums are added in wave
+// order through LDS (a fixed order: the result does not depend on timing).
+// Expert rows past E are replaced by zeros and not written.
+template <int DT>
+struct Mfma16 {
+  typedef bf16x8 V;
+  static __device__ __forceinline__ f32x4 run(V a, V b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Mfma16<MOE_DTYPE_F16> {
+  typedef f16x8 V;
+  static __device__ __forceinline__ f32x4 run(V a, V b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <int DT, int NW, int U>
+__global__ void __launch_bounds__(NW * 64)
+    router_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                       int T, int H, int E, float* __restrict__ logits) {
+  typedef typename Mfma16<DT>::V V;
+  __shared__ f32x4 part[NW][64];
+  const int lane = lane_id();
+  const int wave = (int)threadIdx.x >> 6;
+  const int t0 = (int)blockIdx.x * 16, e0 = (int)blockIdx.y * 16;
+  const int r = lane & 15, q = lane >> 4;
+  const bool ev = e0 + r < E;
+  const uint4* xa = (const uint4*)(x + (long long)min(t0 + r, T - 1) * H) + q;
+  const uint4* wb = (const uint4*)(wr + (long long)min(e0 + r, E - 1) * H) + q;
+  const int nks = H >> 5;  // 32-wide k steps
+  const int ks0 = nks * wave / NW, ks1 = nks * (wave + 1) / NW;
+  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  uint4 a0[U], b0[U], a1[U], b1[U];
+  // batch starting at k step ks: U k steps (past ks1: the last one again,
+  // with a zero activation operand so it adds nothing)
+#define MOE_RLOAD(A, B, ks)                                           \
+  do {                                                                \
+    _Pragma("unroll") for (int u = 0; u < U; ++u) {                   \
+      const int kk = min((ks) + u, ks1 - 1);                          \
+      A[u] = xa[kk * 4];                                              \
+      B[u] = wb[kk * 4];                                              \
+    }                                                                 \
+  } while (0)
+#define MOE_RMFMA(A, B, ks)                                           \
+  do {                                                                \
+    _Pragma("unroll") for (int u = 0; u < U; ++u) {                   \
+      const bool in_ = (ks) + u < ks1;                                \
+      const uint4 av = in_ ? A[u] : zero;                             \
+      const uint4 bv = (in_ && ev) ? B[u] : zero;                     \
+      acc = Mfma16<DT>::run(__builtin_bit_cast(V, av), __builtin_bit_cast(V, bv), acc); \
+    }                                                                 \
+  } while (0)
+  if (ks0 < ks1) {
+    int ks = ks0;
+    MOE_RLOAD(a0, b0, ks);
+    while (true) {
+      if (ks + U < ks1) MOE_RLOAD(a1, b1, ks + U);
+      MOE_RMFMA(a0, b0, ks);
+      ks += U;
+      if (ks >= ks1) break;
+      if (ks + U < ks1) MOE_RLOAD(a0, b0, ks + U);
+      MOE_RMFMA(a1, b1, ks);
+      ks += U;
+      if (ks >= ks1) break;
+    }
+  }
+#undef MOE_RLOAD
+#undef MOE_RMFMA
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4 s = part[0][lane];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) s += part[w][lane];
+    // 16x16 result layout: lane l holds column l % 16, rows 4 * (l / 16) + v
+    if (ev) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = t0 + 4 * q + v;
+        if (t < T) logits[(long long)t * E + e0 + r] = s[v];
+      }
+    }
+  }
+}
+
 namespace {
 
 template <int DT>
@@ -236,6 +332,15 @@ int launch_router_valu(const void* x, const void* wr, int T, int H, int E,
   } while (0)
   MOE_ROUTER(4, 8);
 #undef MOE_ROUTER
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+template <int DT>
+int launch_router_mfma(const void* x, const void* wr, int T, int H, int E, float* logits,
+                       hipStream_t s) {
+  const dim3 grid((T + 15) / 16, (E + 15) / 16);
+  hipLaunchKernelGGL((router_mfma_kernel<DT, 8, 8>), grid, dim3(512), 0, s,
+                     (const uint16_t*)x, (const uint16_t*)wr, T, H, E, logits);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -264,8 +369,9 @@ int route_impl(const void* x, const void* w_router, int act_dtype, const float* 
   if (T == 0) return MOE_OK;
   if (w_router) {
     int st;
-    // matrix tiles for many experts and enough tokens to fill the chip;
-    // the vector kernel otherwise (few experts, or a small decode batch)
+    // staged matrix tiles for many experts and enough tokens to fill the
+    // chip; otherwise 16x16 matrix tiles with operands loaded per lane (few
+    // experts, or a small decode batch), or the vector kernel (float32)
     const bool mfma = act_dtype != MOE_DTYPE_F32 && E >= 128 && E % 128 == 0 &&
                       H % 64 == 0 && T >= 1024;
     if (mfma) {
@@ -284,6 +390,10 @@ int route_impl(const void* x, const void* w_router, int act_dtype, const float* 
       a.I = 0;
       a.K = H;
       st = launch_grouped_gemm(act_dtype, act_dtype, EPI_F32, a, T, s);
+    } else if (act_dtype != MOE_DTYPE_F32 && H % 32 == 0) {
+      st = act_dtype == MOE_DTYPE_F16
+               ? launch_router_mfma<MOE_DTYPE_F16>(x, w_router, T, H, E, logits, s)
+               : launch_router_mfma<MOE_DTYPE_BF16>(x, w_router, T, H, E, logits, s);
     } else if (act_dtype == MOE_DTYPE_F32) {
       st = launch_router_valu<MOE_DTYPE_F32>(x, w_router, T, H, E, logits, s);
     } else if (act_dtype == MOE_DTYPE_F16) {
