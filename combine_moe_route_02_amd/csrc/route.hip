@@ -16,7 +16,7 @@
 // scores, the lowest index.  One wave owns a token; k rounds of a wave-wide
 // uint64 max pick the experts in descending order.
 
-#include "moe_internal.h"
+#include "gemm_tile.h"
 
 namespace moe {
 
@@ -319,6 +319,124 @@ __global__ void __launch_bounds__(NW * 64)
   }
 }
 
+// Router projection for many experts and large batches (E a multiple of
+// 256): one workgroup per 64 tokens scores them against 256 experts, so
+// each activation row is read from memory once.  Copies are staged as in the
+// expert GEMMs (128-byte rows to LDS with global_load_lds, XOR-swizzled
+// chunks), but with three stages and two in flight: this tile's copies are
+// 40 KB and its matrix work per 64-wide k step is a quarter of a 256x256
+// tile's, so with one stage in flight each k step would wait out a whole
+// copy round trip.  Four waves of 64 tokens x 64 experts (2 x 2 tiles of
+// v_mfma_f32_32x32x16), float32 scores.
+template <int DT>
+__global__ void __launch_bounds__(256)
+    router_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                      int T, int H, int E, float* __restrict__ logits) {
+  constexpr int BM = 64, BN = 256, ROWB = 128, NS = 3, NW = 4;
+  constexpr int A_BYTES = BM * ROWB, STAGE = (BM + BN) * ROWB;
+  constexpr int BPW = (BM + BN) / 8 / NW;  // 1 KB copies per wave and stage
+  constexpr int JA = BM / 8 / NW;          // the first JA of them are A rows
+  typedef typename MfmaOp<DT>::V V;
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
+  const int tid = (int)threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lrow = lane & 31, khalf = lane >> 5;
+  const int prow = lane >> 3, pchunk = lane & 7;
+  const int sw_row = dma_swz(lrow) ^ khalf;
+  const int m0 = (int)blockIdx.x * BM, n0 = (int)blockIdx.y * BN;
+  const char* a_tile = uniform_ptr((const char*)(x + (long long)m0 * H));
+  const char* b_tile = uniform_ptr((const char*)(wr + (long long)n0 * H));
+  uint32_t voff[BPW];
+  int ldsoff[BPW];
+#pragma unroll
+  for (int j = 0; j < BPW; ++j) {
+    const int q = wave + NW * j;
+    if (j < JA) {
+      const int row = 8 * q + prow;
+      const int kc = pchunk ^ dma_swz(row);
+      const int grow = min(m0 + row, T - 1);
+      voff[j] = (uint32_t)(grow - m0) * (uint32_t)(H * 2) + (uint32_t)(kc * 16);
+      ldsoff[j] = q * 1024;
+    } else {
+      const int qb = q - BM / 8;
+      const int row = 8 * qb + prow;
+      const int kc = pchunk ^ dma_swz(row);
+      voff[j] = (uint32_t)row * (uint32_t)(H * 2) + (uint32_t)(kc * 16);
+      ldsoff[j] = A_BYTES + qb * 1024;
+    }
+  }
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  const int nk = H / 64;
+  const uint32_t lds0 = lds_addr(smem);
+#define MOE_RISSUE(st)                                                          \
+  do {                                                                          \
+    const uint32_t dst_ = lds0 + ((st) % NS) * STAGE;                           \
+    const char* ak_ = a_tile + (st) * ROWB;                                     \
+    const char* bk_ = b_tile + (st) * ROWB;                                     \
+    _Pragma("unroll") for (int j = 0; j < BPW; ++j)                             \
+      dma16(j < JA ? ak_ : bk_, voff[j], dst_ + ldsoff[j]);                     \
+  } while (0)
+#define MOE_RREAD(As, Bs, s4, FA, FB)                                           \
+  do {                                                                          \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i)                               \
+      FA[i] = *(const V*)((As) + (i * 32 + lrow) * ROWB + (((2 * (s4)) ^ sw_row) << 4)); \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j)                               \
+      FB[j] = *(const V*)((Bs) + (wave * 64 + j * 32 + lrow) * ROWB +           \
+                          (((2 * (s4)) ^ sw_row) << 4));                        \
+  } while (0)
+  MOE_RISSUE(0);
+  if (nk > 1) MOE_RISSUE(1);
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt landed (stage kt+1 may be in flight); after the barrier every
+    // wave's copies of it are visible and every wave is done with stage
+    // kt-1, whose buffer takes stage kt+2
+    if (kt + 1 < nk) wait_vmcnt<BPW>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x7 << 4) | ((0x3F >> 4) << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + 2 < nk) MOE_RISSUE(kt + 2);
+    const char* As = smem + (kt % NS) * STAGE;
+    const char* Bs = As + A_BYTES;
+    V fa0[2], fb0[2], fa1[2], fb1[2];
+    MOE_RREAD(As, Bs, 0, fa0, fb0);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; s4 += 2) {
+      MOE_RREAD(As, Bs, s4 + 1, fa1, fb1);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = MfmaOp<DT>::run(fa0[i], fb0[j], acc[i][j]);
+      if (s4 + 2 < 4) MOE_RREAD(As, Bs, s4 + 2, fa0, fb0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = MfmaOp<DT>::run(fa1[i], fb1[j], acc[i][j]);
+    }
+  }
+#undef MOE_RISSUE
+#undef MOE_RREAD
+  // 32x32 result layout: lane l holds column l % 32, rows 8 * (v / 4) +
+  // 4 * (l / 32) + v % 4
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + i * 32 + (v >> 2) * 8 + khalf * 4 + (v & 3);
+        const int col = n0 + wave * 64 + j * 32 + lrow;
+        if (row < T) logits[(long long)row * E + col] = acc[i][j][v];
+      }
+}
+
 namespace {
 
 template <int DT>
@@ -341,6 +459,17 @@ int launch_router_mfma(const void* x, const void* wr, int T, int H, int E, float
   const dim3 grid((T + 15) / 16, (E + 15) / 16);
   hipLaunchKernelGGL((router_mfma_kernel<DT, 8, 8>), grid, dim3(512), 0, s,
                      (const uint16_t*)x, (const uint16_t*)wr, T, H, E, logits);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+template <int DT>
+int launch_router_dma(const void* x, const void* wr, int T, int H, int E, float* logits,
+                      hipStream_t s) {
+  // per-lane copy offsets are 32-bit: 256 rows of H values must span < 4 GiB
+  if ((long long)256 * H * 2 >= (1ll << 32)) return MOE_ERR_UNSUPPORTED;
+  const dim3 grid((T + 63) / 64, E / 256);
+  hipLaunchKernelGGL((router_dma_kernel<DT>), grid, dim3(256), 0, s, (const uint16_t*)x,
+                     (const uint16_t*)wr, T, H, E, logits);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -374,7 +503,11 @@ int route_impl(const void* x, const void* w_router, int act_dtype, const float* 
     // experts, or a small decode batch), or the vector kernel (float32)
     const bool mfma = act_dtype != MOE_DTYPE_F32 && E >= 128 && E % 128 == 0 &&
                       H % 64 == 0 && T >= 1024;
-    if (mfma) {
+    if (mfma && E % 256 == 0) {
+      st = act_dtype == MOE_DTYPE_F16
+               ? launch_router_dma<MOE_DTYPE_F16>(x, w_router, T, H, E, logits, s)
+               : launch_router_dma<MOE_DTYPE_BF16>(x, w_router, T, H, E, logits, s);
+    } else if (mfma) {
       GemmArgs a{};
       a.A = x;
       a.lda = H;
