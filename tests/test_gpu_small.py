@@ -2,8 +2,10 @@
 
 The shapes span several MFMA tiles with ragged tails, and the edge cases of
 the method: one expert, k = E, all tokens on one expert, empty experts, no
-local expert, a single token, no tokens, mass ties in the scores, and both
-router paths (VALU for few experts, MFMA for many).
+local expert, a single token, no tokens, mass ties in the scores, and every
+router projection kernel (staged MFMA tiles for many experts and large
+batches, per-lane-loaded 16x16 MFMA tiles otherwise, the vector kernel for
+float32 and for rows that are not a multiple of 32).
 """
 
 import numpy as np
@@ -86,6 +88,39 @@ GRID = [
     small("fp8d_threshold", 64, 256, 256, 8, 128, w_dtype=FP8_E4M3, gate=SIGMOID,
           e_end=32, remote=True, min_prob=0.89, fp8d=True, seed_off=56),
 ]
+
+
+# Router projection alone, at the edges of each kernel's tiling: partial token
+# tiles, padded expert tiles, fewer 32-wide k steps than waves, a one-token
+# last tile of the staged kernel, several expert tiles, and 16-bit rows that
+# are not a multiple of 32 (the vector kernel).
+ROUTER_SHAPES = [
+    small("r_mfma16_e8_h96", 33, 96, 8, 2, 64, seed_off=70),
+    small("r_mfma16_e40_f16", 47, 512, 40, 3, 64, act_dtype=F16, seed_off=71),
+    small("r_mfma16_e256_t1", 1, 1024, 256, 8, 64, gate=SIGMOID, seed_off=72),
+    small("r_valu_h200", 20, 200, 8, 2, 64, seed_off=73),
+    small("r_staged_e256_t1025", 1025, 128, 256, 8, 64, gate=SIGMOID, seed_off=74),
+    small("r_staged_e512_f16", 1090, 256, 512, 4, 64, act_dtype=F16, seed_off=75),
+]
+
+
+@pytest.mark.parametrize("cfg", ROUTER_SHAPES, ids=[c.name for c in ROUTER_SHAPES])
+def test_router_projection_paths(cfg):
+    from combine_moe_route_02_amd import MoELayer
+    inp = make_inputs(cfg, "cpu", with_weights=False)
+    st = np_stored(inp)
+    say(f"[gpu] route {cfg.name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k}")
+    lay = MoELayer(spec(cfg), "cuda")
+    dev = to_device(inp)
+    lay.route(dev["x"], dev["w_router"], dev["bias"])
+    torch.cuda.synchronize()
+    logits = lay.logits.cpu().numpy()
+    own = O.router_logits(O.decode(st["x"], cfg.act_dtype),
+                          O.decode(st["w_router"], cfg.act_dtype))
+    assert rel_l2(logits, own) <= TOL_F32
+    idx, w = route(cfg, logits, st["bias"])
+    assert np.array_equal(lay.topk_idx.cpu().numpy(), idx)
+    assert rel_l2(lay.topk_w.cpu().numpy(), w) <= TOL_F32
 
 
 @pytest.mark.parametrize("cfg", GRID, ids=[c.name for c in GRID])
