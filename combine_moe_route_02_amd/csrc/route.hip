@@ -230,9 +230,10 @@ __global__ void __launch_bounds__(256)
 // row l % 16 (a token of x, an expert of Wr) at the 8-element chunk l / 16
 // of every 32-wide k step, so each activation is read once per expert tile
 // and one tile covers all experts when there are at most 16.  The NW waves
-// of the block take consecutive ranges of k steps, keep two batches of U k
-// steps of loads in flight, and their partial 16x16 sums are added in wave
-// order through LDS (a fixed order: the result does not depend on timing).
+// of the block take consecutive ranges of k steps and issue the loads of up
+// to U k steps at once (the block's time is a few load round trips), and
+// their partial 16x16 sums are added in wave order through LDS (a fixed
+// order: the result does not depend on timing).
 // Expert rows past E are replaced by zeros and not written.
 template <int DT>
 struct Mfma16 {
@@ -266,42 +267,25 @@ __global__ void __launch_bounds__(NW * 64)
   const int ks0 = nks * wave / NW, ks1 = nks * (wave + 1) / NW;
   const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  uint4 a0[U], b0[U], a1[U], b1[U];
-  // batch starting at k step ks: U k steps (past ks1: the last one again,
-  // with a zero activation operand so it adds nothing)
-#define MOE_RLOAD(A, B, ks)                                           \
-  do {                                                                \
-    _Pragma("unroll") for (int u = 0; u < U; ++u) {                   \
-      const int kk = min((ks) + u, ks1 - 1);                          \
-      A[u] = xa[kk * 4];                                              \
-      B[u] = wb[kk * 4];                                              \
-    }                                                                 \
-  } while (0)
-#define MOE_RMFMA(A, B, ks)                                           \
-  do {                                                                \
-    _Pragma("unroll") for (int u = 0; u < U; ++u) {                   \
-      const bool in_ = (ks) + u < ks1;                                \
-      const uint4 av = in_ ? A[u] : zero;                             \
-      const uint4 bv = (in_ && ev) ? B[u] : zero;                     \
-      acc = Mfma16<DT>::run(__builtin_bit_cast(V, av), __builtin_bit_cast(V, bv), acc); \
-    }                                                                 \
-  } while (0)
-  if (ks0 < ks1) {
-    int ks = ks0;
-    MOE_RLOAD(a0, b0, ks);
-    while (true) {
-      if (ks + U < ks1) MOE_RLOAD(a1, b1, ks + U);
-      MOE_RMFMA(a0, b0, ks);
-      ks += U;
-      if (ks >= ks1) break;
-      if (ks + U < ks1) MOE_RLOAD(a0, b0, ks + U);
-      MOE_RMFMA(a1, b1, ks);
-      ks += U;
-      if (ks >= ks1) break;
+  // batches of U k steps, all U loads of a batch in flight at once (past
+  // ks1: the last k step again, with zero operands so it adds nothing)
+  for (int ks = ks0; ks < ks1; ks += U) {
+    uint4 a[U], b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = min(ks + u, ks1 - 1);
+      a[u] = xa[kk * 4];
+      b[u] = wb[kk * 4];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the batch issued first
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = ks + u < ks1;
+      const uint4 av = in ? a[u] : zero;
+      const uint4 bv = (in && ev) ? b[u] : zero;
+      acc = Mfma16<DT>::run(__builtin_bit_cast(V, av), __builtin_bit_cast(V, bv), acc);
     }
   }
-#undef MOE_RLOAD
-#undef MOE_RMFMA
   part[wave][lane] = acc;
   __syncthreads();
   if (wave == 0) {
@@ -457,7 +441,7 @@ template <int DT>
 int launch_router_mfma(const void* x, const void* wr, int T, int H, int E, float* logits,
                        hipStream_t s) {
   const dim3 grid((T + 15) / 16, (E + 15) / 16);
-  hipLaunchKernelGGL((router_mfma_kernel<DT, 8, 8>), grid, dim3(512), 0, s,
+  hipLaunchKernelGGL((router_mfma_kernel<DT, 8, 16>), grid, dim3(512), 0, s,
                      (const uint16_t*)x, (const uint16_t*)wr, T, H, E, logits);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
