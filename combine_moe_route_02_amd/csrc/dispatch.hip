@@ -12,6 +12,8 @@
 //
 // Kernels (tile = 256 tokens = 4 waves):
 //   layout_one_tile  hist + scan + slots in one block for T <= 256
+//   layout_few_experts  hist + scan + slots in one launch for E <= 32: every
+//           block counts all picks, then ranks its own tile's
 //   hist    per-tile expert histogram (LDS integer atomics: exact counts)
 //   scan    per-expert prefix over tiles -> tile bases, counts, offsets
 //   slots   rank of each pick among earlier picks of the same expert:
@@ -31,6 +33,9 @@
 namespace moe {
 
 constexpr int TILE = 256;
+// Batches of at most this many picks and at most 32 experts take the
+// one-launch layout (each block counts every pick).
+constexpr long long kFewExpertsMaxPicks = 32768;
 
 __global__ void __launch_bounds__(TILE)
     hist_kernel(const int32_t* __restrict__ idx, int T, int E, int k, int n_tiles,
@@ -229,6 +234,153 @@ __global__ void __launch_bounds__(TILE)
   }
 }
 
+// Whole layout of a multi-tile batch with few experts (E <= EMAX) in one
+// launch, one block per 256-token tile: every block counts all picks itself
+// (16-byte coalesced reads of topk_idx, one counter per expert in each
+// thread, so no atomics pile onto a few hot counters), which gives the
+// totals (counts, offsets) and the picks of each expert before its own tile
+// (its tile base); then its tile's slots exactly as in slots_kernel.  One
+// launch instead of histogram, scan and slots; the same layout.
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+  return v;
+}
+
+// Picks per expert of the whole batch (all) and of the picks before n_bef
+// (bef), in one pass over topk_idx with up to 16 16-byte loads in flight per
+// thread.  Counters are packed eight to a 64-bit register, 8 bits each: a
+// thread sees at most kFewExpertsMaxPicks / TILE = 128 picks.  n_bef is a
+// multiple of 4.
+template <int EMAX>
+__device__ __forceinline__ void add_pick(int e, bool before, uint64_t* all, uint64_t* bef) {
+  // e outside [0, EMAX) (a dropped pick, -1) adds nothing
+  const uint64_t inc = (e >= 0 && e < EMAX) ? 1ull << (8 * (e & 7)) : 0ull;
+#pragma unroll
+  for (int g = 0; g < EMAX / 8; ++g) {
+    const uint64_t x = (e >> 3) == g ? inc : 0ull;
+    all[g] += x;
+    bef[g] += before ? x : 0ull;
+  }
+}
+
+template <int EMAX>
+__device__ __forceinline__ void count_picks(const int32_t* __restrict__ idx, int n_all,
+                                            int n_bef, uint64_t* all, uint64_t* bef) {
+  constexpr int U = 16;
+  const int v_end = n_all >> 2, v_bef = n_bef >> 2;
+  for (int v0 = (int)threadIdx.x; v0 < v_end; v0 += U * TILE) {
+    int4 q[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (v0 + u * TILE < v_end) q[u] = ((const int4*)idx)[v0 + u * TILE];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (v0 + u * TILE >= v_end) break;
+      const bool before = v0 + u * TILE < v_bef;
+      add_pick<EMAX>(q[u].x, before, all, bef);
+      add_pick<EMAX>(q[u].y, before, all, bef);
+      add_pick<EMAX>(q[u].z, before, all, bef);
+      add_pick<EMAX>(q[u].w, before, all, bef);
+    }
+  }
+  // the last n_all % 4 picks (all past n_bef)
+  for (int n = (v_end << 2) + (int)threadIdx.x; n < n_all; n += TILE)
+    add_pick<EMAX>(idx[n], false, all, bef);
+}
+
+template <int KMAX, int EMAX>
+__global__ void __launch_bounds__(TILE)
+    layout_few_experts_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
+                              int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                              int32_t* __restrict__ slot_of, int32_t* __restrict__ row_token) {
+  __shared__ uint64_t lanes_of[4][EMAX];
+  __shared__ int s_cnt[2][4][EMAX];  // [before this tile, all][wave][expert]
+  __shared__ int wbase[4][EMAX];
+  __shared__ int s_base[EMAX];       // offsets[e] + picks of e before this tile
+  const int tile = (int)blockIdx.x;
+  const int wave = (int)threadIdx.x >> 6;
+  const int lane = lane_id();
+  for (int i = threadIdx.x; i < 4 * EMAX; i += TILE) (&lanes_of[0][0])[i] = 0;
+  // 1. this tile's picks (loads issued first, they overlap the count)
+  const int t = tile * TILE + (int)threadIdx.x;
+  const bool valid = t < T;
+  int pk[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) pk[j] = (valid && j < k) ? idx[(long long)t * k + j] : -1;
+  // 2. picks per expert over the batch and before this tile
+  const int n_all = T * k, n_bef = tile * TILE * k;
+  uint64_t all[EMAX / 8], bef[EMAX / 8];
+#pragma unroll
+  for (int g = 0; g < EMAX / 8; ++g) all[g] = bef[g] = 0;
+  count_picks<EMAX>(idx, n_all, n_bef, all, bef);
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    const int a = wave_sum_int((int)((all[e >> 3] >> (8 * (e & 7))) & 0xff));
+    const int b = wave_sum_int((int)((bef[e >> 3] >> (8 * (e & 7))) & 0xff));
+    if (lane == 0) {
+      s_cnt[0][wave][e] = b;
+      s_cnt[1][wave][e] = a;
+    }
+  }
+  const uint64_t bit = 1ull << lane;
+  __syncthreads();  // lanes_of cleared, s_cnt written
+  // lane masks of this tile's picks per wave and expert
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j)
+    if (pk[j] >= 0) atomicOr((unsigned long long*)&lanes_of[wave][pk[j]], bit);
+  // 3. offsets (exclusive scan over experts of the totals) and tile bases
+  if (wave == 0) {
+    const int e = lane;
+    int tot = 0, before = 0;
+    if (e < E) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        before += s_cnt[0][w][e];
+        tot += s_cnt[1][w][e];
+      }
+    }
+    int inc = tot;  // inclusive scan over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(inc, o, MOE_WAVE);
+      if (lane >= o) inc += u;
+    }
+    if (e < E) {
+      s_base[e] = inc - tot + before;
+      if (tile == 0) {
+        counts[e] = tot;
+        offsets[e] = inc - tot;
+        if (e == E - 1) offsets[E] = inc;
+      }
+    }
+  }
+  __syncthreads();  // lane masks and bases complete
+  for (int e = threadIdx.x; e < E; e += TILE) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      wbase[w][e] = run;
+      run += __popcll(lanes_of[w][e]);
+    }
+  }
+  __syncthreads();
+  if (!valid) return;
+  const uint64_t lt = bit - 1;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j >= k) break;
+    const int e = pk[j];
+    if (e < 0) {  // dropped pick: no row
+      slot_of[(long long)t * k + j] = -1;
+      continue;
+    }
+    const int r = s_base[e] + wbase[wave][e] + __popcll(lanes_of[wave][e] & lt);
+    slot_of[(long long)t * k + j] = r;
+    row_token[r] = t;
+  }
+}
+
 // One wave per token; rows of local experts only.  KMAX >= k bounds the
 // unrolled pick loop so the (wave-uniform) row numbers stay in registers.
 template <int KMAX>
@@ -367,6 +519,21 @@ int dispatch_impl(const void* x, int act_dtype, const int32_t* idx, int T, int H
                      s, idx, T, E, k, counts, offsets, slot_of, row_token)
     MOE_BY_K(MOE_LAYOUT1);
 #undef MOE_LAYOUT1
+  } else if (n_tiles > 1 && E <= 32 && (long long)T * k <= kFewExpertsMaxPicks) {
+#define MOE_LAYOUTF(KM)                                                                   \
+  do {                                                                                    \
+    if (E <= 8)                                                                           \
+      hipLaunchKernelGGL((layout_few_experts_kernel<KM, 8>), dim3(n_tiles), dim3(TILE), 0, \
+                         s, idx, T, E, k, counts, offsets, slot_of, row_token);           \
+    else if (E <= 16)                                                                     \
+      hipLaunchKernelGGL((layout_few_experts_kernel<KM, 16>), dim3(n_tiles), dim3(TILE), 0, \
+                         s, idx, T, E, k, counts, offsets, slot_of, row_token);           \
+    else                                                                                  \
+      hipLaunchKernelGGL((layout_few_experts_kernel<KM, 32>), dim3(n_tiles), dim3(TILE), 0, \
+                         s, idx, T, E, k, counts, offsets, slot_of, row_token);           \
+  } while (0)
+    MOE_BY_K(MOE_LAYOUTF);
+#undef MOE_LAYOUTF
   } else {
     if (n_tiles > 0) {
       hipLaunchKernelGGL(hist_kernel, dim3(n_tiles), dim3(TILE), E * sizeof(int), s, idx,

@@ -56,6 +56,11 @@ GRID = [
     small("fp8_multi_mtile", 96, 256, 8, 2, 256, w_dtype=FP8_E4M3, seed_off=13),
     small("fp8_gelu", 80, 256, 8, 2, 256, w_dtype=FP8_E4M3, act=GELU, seed_off=14),
     small("fp8_large_m", 400, 256, 8, 2, 256, w_dtype=FP8_E4M3, seed_off=15),
+    # the one-launch layout for few experts: 17-32 experts, and the largest
+    # batch it takes (32768 picks)
+    small("bf16_e32", 600, 256, 32, 4, 128, gate=SIGMOID, seed_off=19),
+    small("f16_e24", 520, 256, 24, 3, 128, act_dtype=F16, seed_off=20),
+    small("bf16_e32_max_picks", 4096, 256, 32, 8, 128, gate=SIGMOID, seed_off=21),
     # long K: the GEMMs' sparse last round is split over K (parts of 4+ k-steps)
     small("bf16_ksplit", 300, 2048, 8, 2, 1024, seed_off=18),
     # gating variants: temperature, and the minimum-probability threshold
