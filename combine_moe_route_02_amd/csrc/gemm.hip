@@ -665,10 +665,12 @@ int device_cus() {
 // Persistent grid: no more workgroups than can be resident at once (so the
 // XCD placement i % 8 holds for all of them) and no more than the tile count
 // can use; always a multiple of 8.
+// occ: the caller's cache of the kernel's occupancy (one per kernel: every
+// kernel here has the same function type, so a cache keyed on the type would
+// be shared between them).
 template <typename Kern>
 dim3 persistent_grid(Kern kernel, int threads, GemmArgs& a, int max_rows, int BM, int BN,
-                     int gm) {
-  static int occ = 0;  // one cache per kernel instantiation
+                     int gm, int& occ) {
   if (occ == 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess ||
@@ -696,9 +698,17 @@ int run_mfma(GemmArgs a, int max_rows, int gm, hipStream_t s) {
     return MOE_ERR_UNSUPPORTED;
   if (a.offsets && a.n_groups > 1024) return MOE_ERR_UNSUPPORTED;
   auto kern = grouped_gemm_mfma<DT, WK, EPI, BM, BN, WM, WN>;
-  const dim3 grid = persistent_grid(kern, WM * WN * 64, a, max_rows, BM, BN, gm);
+  static int occ = 0;
+  const dim3 grid = persistent_grid(kern, WM * WN * 64, a, max_rows, BM, BN, gm, occ);
   hipLaunchKernelGGL(kern, grid, dim3(WM * WN * 64), 0, s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+template <int DT, int EPI, int BM, int BN, int WM, int WN>
+dim3 dma_grid(GemmArgs& a, int max_rows, int gm) {
+  static int occ = 0;
+  return persistent_grid(grouped_gemm_dma<DT, EPI, BM, BN, WM, WN>, WM * WN * 64, a, max_rows,
+                         BM, BN, gm, occ);
 }
 
 template <int DT, int EPI, int BM, int BN, int WM, int WN>
@@ -708,7 +718,7 @@ int run_dma(GemmArgs a, int max_rows, int gm, hipStream_t s) {
   if ((long long)a.Nb * a.ldb * 2 >= (1ll << 32)) return MOE_ERR_UNSUPPORTED;
   if (a.offsets && a.n_groups > 1024) return MOE_ERR_UNSUPPORTED;
   auto kern = grouped_gemm_dma<DT, EPI, BM, BN, WM, WN>;
-  const dim3 grid = persistent_grid(kern, WM * WN * 64, a, max_rows, BM, BN, gm);
+  const dim3 grid = dma_grid<DT, EPI, BM, BN, WM, WN>(a, max_rows, gm);
   // the k-split needs one slot per workgroup and one counter per tile slot
   typedef DmaTile<DT, EPI, BM, BN, WM, WN> Tile;
   // (slots are counted in units of a 256x256 tile's accumulators)
@@ -729,7 +739,8 @@ int run_fp8s(GemmArgs a, int max_rows, hipStream_t s) {
   if ((long long)a.Nb * a.ldb >= (1ll << 32)) return MOE_ERR_UNSUPPORTED;
   if (a.offsets && a.n_groups > 1024) return MOE_ERR_UNSUPPORTED;
   auto kern = grouped_gemm_fp8s<DT, EPI, A8>;
-  const dim3 grid = persistent_grid(kern, 256, a, max_rows, 32, 256, 1);
+  static int occ = 0;
+  const dim3 grid = persistent_grid(kern, 256, a, max_rows, 32, 256, 1, occ);
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
@@ -742,22 +753,14 @@ struct TileShape {
   float eff;
 };
 
-template <int DT, int WK, int EPI>
-int pick_tile(GemmArgs a, int max_rows, hipStream_t s) {
-  if (EPI == EPI_F32) {
-    // router logits: one n-tile of 256 experts reads each token row once
-    if (WK == W_SAME && a.Nb % 256 == 0) return run_dma<DT, EPI, 64, 256, 1, 4>(a, max_rows, 4, s);
-    if (WK == W_SAME) return run_dma<DT, EPI, 64, 128, 2, 2>(a, max_rows, 4, s);
-    return run_mfma<DT, WK, EPI, 64, 128, 2, 2>(a, max_rows, 4, s);
-  }
+// Tile height of the many-rows path (256 or 128): a cost model that counts
+// rounds of workgroups, with the last partial round split over k when a
+// workspace is attached and it is at most half full.
+template <int WK>
+int choose_bm(const GemmArgs& a, int max_rows) {
   const int groups = a.offsets ? a.n_groups : 1;
   const int rows = a.offsets ? max_rows : a.dense_M;
   const double avg = (double)rows / (groups > 0 ? groups : 1);
-  if (avg <= 48.0) {
-    if constexpr (WK == W_FP8 && DT == MOE_DTYPE_BF16 && EPI != EPI_F32)
-      return run_fp8s<DT, EPI>(a, max_rows, s);
-    return run_mfma<DT, WK, EPI, 32, 256, 1, 4>(a, max_rows, 1, s);
-  }
   const TileShape shapes[2] = {{256, 256, 1.0f}, {128, 256, 0.8f}};
   int best = 0;
   double best_t = 1e300;
@@ -780,8 +783,31 @@ int pick_tile(GemmArgs a, int max_rows, hipStream_t s) {
       best = c;
     }
   }
+  return shapes[best].BM;
+}
+
+// Few rows per group (decode batches) take the 32-row tiles.
+inline bool few_rows(const GemmArgs& a, int max_rows) {
+  const int groups = a.offsets ? a.n_groups : 1;
+  const int rows = a.offsets ? max_rows : a.dense_M;
+  return (double)rows / (groups > 0 ? groups : 1) <= 48.0;
+}
+
+template <int DT, int WK, int EPI>
+int pick_tile(GemmArgs a, int max_rows, hipStream_t s) {
+  if (EPI == EPI_F32) {
+    // router logits: one n-tile of 256 experts reads each token row once
+    if (WK == W_SAME && a.Nb % 256 == 0) return run_dma<DT, EPI, 64, 256, 1, 4>(a, max_rows, 4, s);
+    if (WK == W_SAME) return run_dma<DT, EPI, 64, 128, 2, 2>(a, max_rows, 4, s);
+    return run_mfma<DT, WK, EPI, 64, 128, 2, 2>(a, max_rows, 4, s);
+  }
+  if (few_rows(a, max_rows)) {
+    if constexpr (WK == W_FP8 && DT == MOE_DTYPE_BF16 && EPI != EPI_F32)
+      return run_fp8s<DT, EPI>(a, max_rows, s);
+    return run_mfma<DT, WK, EPI, 32, 256, 1, 4>(a, max_rows, 1, s);
+  }
   if constexpr (WK == W_SAME) {
-    if (best == 0) return run_dma<DT, EPI, 256, 256, 2, 2>(a, max_rows, 8, s);
+    if (choose_bm<WK>(a, max_rows) == 256) return run_dma<DT, EPI, 256, 256, 2, 2>(a, max_rows, 8, s);
     return run_dma<DT, EPI, 128, 256, 2, 2>(a, max_rows, 8, s);
   } else {
     return run_mfma<DT, WK, EPI, 128, 256, 2, 2>(a, max_rows, 8, s);
@@ -793,7 +819,8 @@ int run_f32(GemmArgs a, int max_rows, hipStream_t s) {
   if (a.Nb % 64 || a.K % 16) return MOE_ERR_UNSUPPORTED;
   if (a.offsets && a.n_groups > 1024) return MOE_ERR_UNSUPPORTED;
   auto kern = grouped_gemm_f32<EPI>;
-  const dim3 grid = persistent_grid(kern, 256, a, max_rows, 64, 64, 4);
+  static int occ = 0;
+  const dim3 grid = persistent_grid(kern, 256, a, max_rows, 64, 64, 4, occ);
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
