@@ -303,16 +303,17 @@ __device__ __forceinline__ long fp8x8_as_long(uint32_t lo, uint32_t hi) {
   return (long)(((unsigned long)hi << 32) | lo);
 }
 
-template <int DT, int EPI, bool A8 = false>
+template <int DT, int EPI, bool A8 = false, int TN = 2>
 struct Fp8SmallTile {
   static_assert(DT == MOE_DTYPE_BF16, "fp8 weights pair with bf16 activations");
-  static constexpr int BM = 32, BN = 256, BK = 128, NS = 3, NW = 4;
+  static_assert(TN == 2 || (TN == 1 && EPI != EPI_SWIGLU), "SwiGLU pairs two column groups");
+  static constexpr int BM = 32, BN = 128 * TN, BK = 128, NS = 3, NW = 4;
   static constexpr int NT = NW * 64;
-  static constexpr int TN = 2;                        // 32-column groups per wave
+  static constexpr int WC = 32 * TN;                  // columns per wave
   static constexpr int A_ROWB = A8 ? BK : BK * 2;     // 128 B (fp8) or 256 B (16-bit)
   static constexpr int B_ROWB = BK;                   // 128 B (fp8)
   static constexpr int A_BYTES = BM * A_ROWB, B_BYTES = BN * B_ROWB;
-  static constexpr int STAGE = A_BYTES + B_BYTES;     // 40 KB
+  static constexpr int STAGE = A_BYTES + B_BYTES;     // 40 KB (24 KB at TN = 1)
   static constexpr int A_BLK = A_BYTES / 1024;        // blocks of 4 (fp8: 8) A rows
   static constexpr int B_BLK = B_BYTES / 1024;        // blocks of 8 B rows
   static constexpr int BPW = (A_BLK + B_BLK) / NW;
@@ -376,7 +377,7 @@ struct Fp8SmallTile {
     for (int j = 0; j < TN; ++j) {
       int n;
       if (EPI == EPI_SWIGLU) n = (j ? p.I : 0) + n0h + wn * 32;
-      else n = n0 + wn * 64 + j * 32;
+      else n = n0 + wn * WC + j * 32;
       srow[j] = p.Bscale + (long long)ti.g * p.strideS + (long long)(n >> 7) * (p.K >> 7);
     }
 
@@ -428,7 +429,7 @@ do {                                                                            
           const long a = fp8x8_as_long(a8.x, a8.y);
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
-            const int brow = wn * 64 + j * 32 + lrow;
+            const int brow = wn * WC + j * 32 + lrow;
             const uint2 q8 = *(const uint2*)(Bs + brow * B_ROWB +
                                             ((s8 ^ ((brow >> 1) & 7)) << 4) + khalf * 8);
             part[j] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(
@@ -438,7 +439,7 @@ do {                                                                            
           const V a = *(const V*)(As + lrow * A_ROWB + (((2 * s8 + khalf) ^ (lrow & 15)) << 4));
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
-            const int brow = wn * 64 + j * 32 + lrow;
+            const int brow = wn * WC + j * 32 + lrow;
             const uint2 q8 = *(const uint2*)(Bs + brow * B_ROWB +
                                             ((s8 ^ ((brow >> 1) & 7)) << 4) + khalf * 8);
             part[j] = MfmaOp<DT>::run(a, decode_fp8x8(q8.x, q8.y), part[j]);
@@ -473,16 +474,16 @@ do {                                                                            
         for (int j = 0; j < TN; ++j) {
           float y = acc[j][v];
           if (EPI == EPI_GELU) y = gelu_erf16(y);
-          C[crow * p.ldc + n0 + wn * 64 + j * 32 + lrow] = Act<DT>::store(y);
+          C[crow * p.ldc + n0 + wn * WC + j * 32 + lrow] = Act<DT>::store(y);
         }
       }
     }
   }
 };
 
-template <int DT, int EPI, bool A8 = false>
+template <int DT, int EPI, bool A8 = false, int TN = 2>
 __global__ void __launch_bounds__(256) grouped_gemm_fp8s(GemmArgs p) {
-  typedef Fp8SmallTile<DT, EPI, A8> Tile;
+  typedef Fp8SmallTile<DT, EPI, A8, TN> Tile;
   __shared__ __attribute__((aligned(1024))) char smem[Tile::SMEM];
   __shared__ int s_pre[1024];
   __shared__ int s_scan[Tile::NT];
@@ -733,16 +734,31 @@ int run_dma(GemmArgs a, int max_rows, int gm, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+template <int DT, int EPI, bool A8, int TN>
+int launch_fp8s(GemmArgs a, int max_rows, hipStream_t s) {
+  auto kern = grouped_gemm_fp8s<DT, EPI, A8, TN>;
+  static int occ = 0;
+  const dim3 grid = persistent_grid(kern, 256, a, max_rows, 32, 128 * TN, 1, occ);
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// Tiles of 256 columns, or of 128 where that fills the last round: with one
+// 32-row tile per group (the decode regime), t tiles of 256 columns take
+// ceil(t / G) rounds on G workgroups and 2t tiles of 128 columns half as long
+// each (SwiGLU keeps 256: a wave pairs gate and up columns).
 template <int DT, int EPI, bool A8 = false>
 int run_fp8s(GemmArgs a, int max_rows, hipStream_t s) {
   if (a.Nb % 256 || a.K % 128) return MOE_ERR_UNSUPPORTED;
   if ((long long)a.Nb * a.ldb >= (1ll << 32)) return MOE_ERR_UNSUPPORTED;
   if (a.offsets && a.n_groups > 1024) return MOE_ERR_UNSUPPORTED;
-  auto kern = grouped_gemm_fp8s<DT, EPI, A8>;
-  static int occ = 0;
-  const dim3 grid = persistent_grid(kern, 256, a, max_rows, 32, 256, 1, occ);
-  hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, a);
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  if constexpr (EPI != EPI_SWIGLU) {
+    const long long G = device_cus();
+    const long long t = (long long)(a.offsets ? a.n_groups : 1) * (a.Nb / 256);
+    if ((2 * t + G - 1) / G < 2 * ((t + G - 1) / G))
+      return launch_fp8s<DT, EPI, A8, 1>(a, max_rows, s);
+  }
+  return launch_fp8s<DT, EPI, A8, 2>(a, max_rows, s);
 }
 
 // Relative MFMA efficiency of each tile shape (larger wave tiles need fewer
