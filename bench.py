@@ -459,12 +459,25 @@ def pmc_summary(fetch_csv, write_csv, out_path, calib_mib, workload, extra=""):
     fetch = _per_kernel(_counter_rows(fetch_csv), "FETCH_SIZE")
     write = _per_kernel(_counter_rows(write_csv), "WRITE_SIZE")
     # the calibration copy is the runtime's buffer copy of calib_mib MiB
-    # (b.copy_(a) on contiguous uint8 tensors); take its largest dispatch
+    # (b.copy_(a) on contiguous uint8 tensors).  Input generation copies too,
+    # some of them larger, so it is found by its WRITE_SIZE (exact for a
+    # copy: calib_mib MiB) and its FETCH_SIZE taken from the copy at the same
+    # position of the other run (both runs launch the same sequence).
     true_kib = calib_mib * 1024.0
-    cf = max(fetch.get("__amd_rocclr_copyBuffer", [0.0]))
-    cw = max(write.get("__amd_rocclr_copyBuffer", [0.0]))
-    if cf <= 0 or cw <= 0:
+
+    def copies(path, counter):
+        rows = [r for r in _counter_rows(path)
+                if r["Counter_Name"] == counter and r["Kernel_Name"] == "__amd_rocclr_copyBuffer"]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        return [float(r["Counter_Value"]) for r in rows]
+    cw_all = copies(write_csv, "WRITE_SIZE")
+    cf_all = copies(fetch_csv, "FETCH_SIZE")
+    if not cw_all or len(cw_all) != len(cf_all):
         raise SystemExit("calibration copy not found in the counter CSVs")
+    i = min(range(len(cw_all)), key=lambda j: abs(cw_all[j] - true_kib))
+    if abs(cw_all[i] - true_kib) > 0.01 * true_kib:
+        raise SystemExit("no copy of the calibration size in the WRITE_SIZE run")
+    cf, cw = cf_all[i], cw_all[i]
     f_scale, w_scale = true_kib / cf, true_kib / cw
     def is_gemm1(name):
         if "fused_layer" in name:
@@ -499,6 +512,18 @@ def pmc_summary(fetch_csv, write_csv, out_path, calib_mib, workload, extra=""):
         rec.setdefault("hbm_bytes_per_launch", hbm)
         rec.setdefault("fetch_kib_per_launch", fk)
         rec.setdefault("write_kib_per_launch", wk)
+    # every kernel of the library, for the HBM rates of route, dispatch and
+    # combine (divide by the kernel-trace medians of the same workload)
+    lines.append("# every library kernel: median FETCH_SIZE / WRITE_SIZE KiB per dispatch "
+                 "and the scaled HBM bytes")
+    for k in sorted(fetch):
+        if not k.startswith(("void moe::", "moe::")):
+            continue
+        fk = float(np.median(fetch[k]))
+        wk = float(np.median(write.get(k, [0.0])))
+        hbm = (fk * f_scale + wk * w_scale) * 1024.0
+        lines.append(f"#   {k[:100]}: {len(fetch[k])} dispatches, FETCH {fk:.0f} KiB, "
+                     f"WRITE {wk:.0f} KiB, HBM {hbm / 1e6:.2f} MB")
     lines.append(f"source_hash = {source_hash('fused' if extra else 'gemm1')}")
     for key, v in rec.items():
         lines.append(f"{key} = {v:.0f}")
