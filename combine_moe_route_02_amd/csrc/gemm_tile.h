@@ -432,6 +432,34 @@ do {                                                                            
     _Pragma("unroll") for (int j = 0; j < TN; ++j)                                 \
       acc[i][j] = MfmaOp<DT>::run(FA[i], FB[j], acc[i][j]);                        \
 } while (0)
+// Fragment read r (r < TM: A block r, else B block r - TM) of substep s4
+// of a stage, and the MFMA after which it is issued: the TM + TN reads are
+// spread evenly over the TM * TN MFMAs of a substep.
+#define MOE_READ1(stage, s4, r, NA, NB)                                            \
+do {                                                                             \
+    const char* As_ = smem + (stage) * STAGE;                                      \
+    const char* Bs_ = As_ + A_BYTES;                                               \
+    if ((r) < TM)                                                                  \
+      NA[r] = *(const V*)(As_ + (wm * WTM + (r) * 32 + lrow) * ROWB + (((2 * (s4)) ^ sw_row) << 4)); \
+    else                                                                           \
+      NB[(r) - TM] = *(const V*)(Bs_ + (wn * WTN + ((r) - TM) * 32 + lrow) * ROWB +       \
+                                 (((2 * (s4)) ^ sw_row) << 4));                    \
+} while (0)
+#define MOE_READ_AT(r) (((r) + 1) * (TM * TN) / (TM + TN) > 0 ? ((r) + 1) * (TM * TN) / (TM + TN) - 1 : 0)
+// The MFMAs of one substep (operands FA, FB) with the fragment reads of
+// substep s4 of a stage (into NA, NB) interleaved: a burst of all the reads
+// before the MFMAs fills the LDS queue and stalls the wave's issue while the
+// matrix pipe waits (measured 1-3% slower per GEMM than this order, same
+// sums).
+#define MOE_MFMAS_READ(FA, FB, stage, s4, NA, NB)                                  \
+do {                                                                             \
+    _Pragma("unroll") for (int q_ = 0; q_ < TM * TN; ++q_) {                      \
+      acc[q_ / TN][q_ % TN] = MfmaOp<DT>::run(FA[q_ / TN], FB[q_ % TN], acc[q_ / TN][q_ % TN]); \
+      _Pragma("unroll") for (int r_ = 0; r_ < TM + TN; ++r_)                        \
+        if (MOE_READ_AT(r_) == q_) MOE_READ1(stage, s4, r_, NA, NB);                \
+      __builtin_amdgcn_sched_barrier(0);                                           \
+    }                                                                              \
+} while (0)
 // The next stage becomes readable: this wave's copies of it are done (only
 // the n_pf prefetch groups issued after them may be in flight), its LDS
 // reads are done, and a barrier covers the other waves' copies and reads.
@@ -492,31 +520,24 @@ do {                                                                            
     // Loop invariant at the top of k-step kt: stage kt is visible and its
     // substep 0 is in (xa, xb) (reads possibly in flight); stage kt+1 has
     // been issued.  Substeps 1..3 are read one substep ahead of their
-    // MFMAs.  During substep 3 the next stage is made visible, its substep 0
-    // read, and stage kt's buffer (read by every wave by then) refilled
-    // with stage kt+2, one copy per MFMA so the issue slots overlap the
-    // matrix pipe.  The body is straight-line so the compiler's own LDS
+    // MFMAs, interleaved with them.  Before the MFMAs of substep 3 the next
+    // stage is made visible; those MFMAs then carry the reads of its
+    // substep 0 and the refill of stage kt's buffer (read by every wave by
+    // then) with stage kt+2, one copy per MFMA, so the issue slots overlap
+    // the matrix pipe.  The body is straight-line so the compiler's own LDS
     // wait counts stay exact.
     int kt = 0;
     for (; kt < nk - 2; ++kt) {
       const int st = kt & 1;
-      MOE_READ(st, 1, ya, yb);
+      MOE_MFMAS_READ(xa, xb, st, 1, ya, yb);
       MOE_PHASE();
-      MOE_MFMAS(xa, xb);
+      MOE_MFMAS_READ(ya, yb, st, 2, xa, xb);
       MOE_PHASE();
-      MOE_READ(st, 2, xa, xb);
-      MOE_PHASE();
-      MOE_MFMAS(ya, yb);
-      MOE_PHASE();
-      MOE_READ(st, 3, ya, yb);
-      MOE_PHASE();
-      MOE_MFMAS(xa, xb);
+      MOE_MFMAS_READ(xa, xb, st, 3, ya, yb);
       MOE_PHASE();
       // prefetch groups issued after stage kt+1's copies: the prologue's two
       // for kt = 0, else the one issued with them (if any)
       MOE_STAGE_READY(kt == 0 ? npf0 : (kt + 3 < nk));
-      MOE_READ(st ^ 1, 0, xa, xb);
-      MOE_PHASE();
       {
         const uint32_t dst_ = lds0 + st * STAGE;
         const int kofs_ = MOE_KOFS(kt + 2);
@@ -527,6 +548,9 @@ do {                                                                            
 #pragma unroll
         for (int q = 0; q < MF; ++q) {
           acc[q / TN][q % TN] = MfmaOp<DT>::run(ya[q / TN], yb[q % TN], acc[q / TN][q % TN]);
+#pragma unroll
+          for (int r_ = 0; r_ < TM + TN; ++r_)
+            if (MOE_READ_AT(r_) == q) MOE_READ1(st ^ 1, 0, r_, xa, xb);
 #pragma unroll
           for (int r = 0; r < (BPW + MF - 1) / MF; ++r) {
             const int j = (q / EVERY) * ((BPW + MF - 1) / MF) + r;
@@ -565,6 +589,9 @@ do {                                                                            
     }
 #undef MOE_PHASE
 #undef MOE_READ
+#undef MOE_MFMAS_READ
+#undef MOE_READ1
+#undef MOE_READ_AT
 #undef MOE_MFMAS
 #undef MOE_STAGE_READY
 #undef MOE_ISSUE
