@@ -15,13 +15,15 @@
 // weights are read from HBM about once, and a band's activation rows are
 // reused across its n-tiles.
 //
-// 16-bit weights (DmaTile): global -> LDS directly, four stages of BK = 32.
+// 16-bit weights (DmaTile): global -> LDS directly, two stages of BK = 64;
+// each wave owns a (BM/WM) x (BN/WN) accumulator block of 16x16 MFMA tiles
+// (v_mfma_f32_16x16x32_{bf16,f16}).
 // fp8 weights (register-staged kernel below): BK = 64; global -> registers
 // -> LDS with a two-buffer ring and one barrier per k-step; 16-byte chunks
 // are stored XOR-swizzled (chunk ^ (row & 7)) so that the ds_read_b128 of an
 // MFMA operand (32 rows, same k-chunk) touches every bank group once.  Each
 // wave owns a (BM/WM) x (BN/WN) accumulator block of 32x32 MFMA tiles
-// (v_mfma_f32_32x32x16_{bf16,f16}: 8 values of K per lane per operand).
+// (v_mfma_f32_32x32x16: 8 values of K per lane per operand).
 //
 // Epilogues: plain store in the activation dtype, SwiGLU (the B tile
 // interleaves 32-row groups of gate and up rows so a wave holds both halves

@@ -132,6 +132,41 @@ struct MfmaOp<MOE_DTYPE_F16> {
   }
 };
 
+// MFMA instruction of a tile: 32x32x16 (MI = 32, 16 results per lane) or
+// 16x16x32 (MI = 16, 4 results per lane); both take 8 16-bit values of K
+// per lane and operand.  On gfx950 the two give bit-identical sums over the
+// same K order (checked on full expert-FFN GEMMs); the 16x16x32 form is the
+// faster one in the tiles below: a k-step is 2 substeps of 64 short MFMAs
+// instead of 4 of 16 long ones, which leaves finer slots between them for
+// the LDS reads and copies.
+template <int DT, int MI>
+struct MfmaT;
+template <int DT>
+struct MfmaT<DT, 32> {
+  typedef typename MfmaOp<DT>::V V;
+  typedef f32x16 Acc;
+  static constexpr int NV = 16;
+  static __device__ __forceinline__ Acc run(V a, V b, Acc c) { return MfmaOp<DT>::run(a, b, c); }
+};
+template <>
+struct MfmaT<MOE_DTYPE_BF16, 16> {
+  typedef bf16x8 V;
+  typedef f32x4 Acc;
+  static constexpr int NV = 4;
+  static __device__ __forceinline__ Acc run(V a, V b, Acc c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct MfmaT<MOE_DTYPE_F16, 16> {
+  typedef f16x8 V;
+  typedef f32x4 Acc;
+  static constexpr int NV = 4;
+  static __device__ __forceinline__ Acc run(V a, V b, Acc c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
 // One accumulator value read into a vector register at this point of the
 // program (a plain use lets the compiler copy every accumulator out at once).
 __device__ __forceinline__ float acc_read(float a) {
@@ -171,8 +206,8 @@ __device__ __forceinline__ float gelu_erf16(float a) {
 //
 // Stage layout: rows of 128 bytes (64 values, one full cache line of a
 // K-contiguous row); 16-byte chunk kc of row r sits at chunk kc ^ dma_swz(r),
-// so the 32 rows an MFMA operand read touches (same logical chunk) spread
-// over all bank groups.  One wave instruction fills one 1 KB block (8 rows):
+// so the 16 or 32 rows an MFMA operand read touches (same logical chunk)
+// spread over all bank groups.  One wave instruction fills one 1 KB block (8 rows):
 // lane p writes row p/8, physical chunk p%8, and fetches the logical chunk
 // that belongs there.  Whole 128-byte lines per row matter: the same bytes
 // fetched as 64-byte halves of twice as many lines take twice as many L2
@@ -182,8 +217,9 @@ __device__ __forceinline__ float gelu_erf16(float a) {
 // stage's loads and then a barrier makes every wave's loads visible.
 // ---------------------------------------------------------------------------
 
-// LDS chunk swizzle of a 128-byte row: conflict-free for the 32 rows of an
-// MFMA operand read whether the LDS serves 8 lanes x 16 B (32 banks) or
+// LDS chunk swizzle of a 128-byte row: conflict-free for the 32 rows x 2
+// chunks of a 32x32x16 operand read and the 16 rows x 4 chunks of a
+// 16x16x32 one, whether the LDS serves 8 lanes x 16 B (32 banks) or
 // 16 lanes x 16 B (64 banks) per cycle.
 __device__ __forceinline__ int dma_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
@@ -259,7 +295,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // in its own slot, and the last of the `parts` workgroups to arrive adds all
 // slots in part order (so the result does not depend on arrival order) and
 // runs the epilogue.  Part s's slot is slot0 + s * slot_step floats; each
-// thread owns a contiguous run of TM * TN * 16 floats in it.
+// thread owns a contiguous run of NACC floats in it (the tile's accumulators
+// per thread: 256 for a 256x256 tile).
 struct KSplit {
   int k0, nk;
   int parts, part;
@@ -274,13 +311,17 @@ struct KSplit {
 // a_gather, at row a_gather[r] (the fused kernel reads token rows of x
 // through the layout map instead of a gathered copy).  smem must hold
 // SMEM bytes; all threads of the block call it.  K must be a multiple of 64.
-template <int DT, int EPI, int BM, int BN, int WM, int WN>
+template <int DT, int EPI, int BM, int BN, int WM, int WN, int MI = 16>
 struct DmaTile {
+  typedef MfmaT<DT, MI> MO;
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * 64;
   static constexpr int BK = 64, NS = 2;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
-  static constexpr int TM = WTM / 32, TN = WTN / 32;
+  static constexpr int TM = WTM / MI, TN = WTN / MI;    // MI x MI blocks per wave
+  static constexpr int NV = MO::NV;                    // results per lane and block
+  static constexpr int KSUB = 512 / MI;                // K of one MFMA: 16 or 32
+  static constexpr int NSUB = BK / KSUB;               // substeps per k-step: 4 or 2
   static constexpr int ROWB = BK * 2;  // bytes per staged row
   static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
   static constexpr int STAGE = A_BYTES + B_BYTES;
@@ -292,26 +333,29 @@ struct DmaTile {
   static constexpr int SMEM = NS * STAGE + NW * 256;
   static_assert(A_BLK % NW == 0 && B_BLK % NW == 0, "blocks per wave");
   static_assert(TM >= 1 && TN >= 1, "tile");
-  static_assert(EPI != EPI_SWIGLU || (TN % 2) == 0, "swiglu pairs");
+  static_assert(EPI != EPI_SWIGLU || (TN % (MI == 32 ? 2 : 4)) == 0, "swiglu pairs");
   static_assert(BPW + 2 * NPF < 64, "vmcnt range");
+  static_assert(MI == 32 || MI == 16, "MFMA shape");
 
-  static constexpr int NACC = TM * TN * 16;  // accumulators per thread
+  static constexpr int NACC = TM * TN * NV;  // accumulators per thread
   static constexpr long long SLOT = (long long)NT * NACC;  // floats per split slot
 
   __device__ static __forceinline__ void run(const GemmArgs& p, const TileInfo& ti, int nt,
                                              char* smem, const int32_t* a_gather,
                                              const KSplit* ks = nullptr) {
-    typedef typename MfmaOp<DT>::V V;
+    typedef typename MO::V V;
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
-    const int lrow = lane & 31;
-    const int khalf = lane >> 5;
+    const int lrow = lane & (MI - 1);   // operand row of this lane in a block
+    const int kgrp = lane / MI;         // its 8-value group of the substep's K
     const int prow = lane >> 3, pchunk = lane & 7;  // DMA lane -> (row, chunk)
-    // MFMA operand read of k16 substep s: logical chunk 2s + khalf of a row
-    // whose swizzle is that of lrow (tile rows start at multiples of 32).
-    const int sw_row = dma_swz(lrow) ^ khalf;  // chunk 2 * s4 + khalf -> ^ sw_row
+    // MFMA operand read of substep s: logical 16-byte chunk (KSUB / 8) * s +
+    // kgrp of a row whose swizzle is that of lrow (blocks start at multiples
+    // of MI, and the swizzle depends on the row mod 16).  KSUB / 8 * s has
+    // no bits in common with kgrp, so the chunk is (KSUB / 8 * s) ^ sw_row.
+    const int sw_row = dma_swz(lrow) ^ kgrp;
 
     const int a_sub = p.a_local ? ti.base : 0;
     const int c_sub = p.c_local ? ti.base : 0;
@@ -397,13 +441,13 @@ struct DmaTile {
       }
     }
 
-    f32x16 acc[TM][TN];
+    typename MO::Acc acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+        for (int v = 0; v < NV; ++v) acc[i][j][v] = 0.0f;
 
     const int nk = ks ? ks->nk : p.K / BK;      // k-steps of this share
     const int kbase = ks ? ks->k0 : 0;          // its first k-step
@@ -416,21 +460,21 @@ struct DmaTile {
     const int skew = MOE_SKEW(nt, nk);
 #define MOE_KOFS(st) ((kbase + (((st) + skew) < nk ? (st) + skew : (st) + skew - nk)) * ROWB)
 
-// Fragments of k16 substep s4 of a stage into FA/FB.
+// Fragments of substep s4 of a stage into FA/FB.
 #define MOE_READ(stage, s4, FA, FB)                                                \
 do {                                                                             \
     const char* As_ = smem + (stage) * STAGE;                                      \
     const char* Bs_ = As_ + A_BYTES;                                               \
     _Pragma("unroll") for (int i = 0; i < TM; ++i)                                 \
-      FA[i] = *(const V*)(As_ + (wm * WTM + i * 32 + lrow) * ROWB + (((2 * (s4)) ^ sw_row) << 4)); \
+      FA[i] = *(const V*)(As_ + (wm * WTM + i * MI + lrow) * ROWB + ((((KSUB / 8) * (s4)) ^ sw_row) << 4)); \
     _Pragma("unroll") for (int j = 0; j < TN; ++j)                                 \
-      FB[j] = *(const V*)(Bs_ + (wn * WTN + j * 32 + lrow) * ROWB + (((2 * (s4)) ^ sw_row) << 4)); \
+      FB[j] = *(const V*)(Bs_ + (wn * WTN + j * MI + lrow) * ROWB + ((((KSUB / 8) * (s4)) ^ sw_row) << 4)); \
 } while (0)
 #define MOE_MFMAS(FA, FB)                                                          \
 do {                                                                             \
     _Pragma("unroll") for (int i = 0; i < TM; ++i)                                 \
     _Pragma("unroll") for (int j = 0; j < TN; ++j)                                 \
-      acc[i][j] = MfmaOp<DT>::run(FA[i], FB[j], acc[i][j]);                        \
+      acc[i][j] = MO::run(FA[i], FB[j], acc[i][j]);                                \
 } while (0)
 // Fragment read r (r < TM: A block r, else B block r - TM) of substep s4
 // of a stage, and the MFMA after which it is issued: the TM + TN reads are
@@ -440,10 +484,10 @@ do {                                                                            
     const char* As_ = smem + (stage) * STAGE;                                      \
     const char* Bs_ = As_ + A_BYTES;                                               \
     if ((r) < TM)                                                                  \
-      NA[r] = *(const V*)(As_ + (wm * WTM + (r) * 32 + lrow) * ROWB + (((2 * (s4)) ^ sw_row) << 4)); \
+      NA[r] = *(const V*)(As_ + (wm * WTM + (r) * MI + lrow) * ROWB + ((((KSUB / 8) * (s4)) ^ sw_row) << 4)); \
     else                                                                           \
-      NB[(r) - TM] = *(const V*)(Bs_ + (wn * WTN + ((r) - TM) * 32 + lrow) * ROWB +       \
-                                 (((2 * (s4)) ^ sw_row) << 4));                    \
+      NB[(r) - TM] = *(const V*)(Bs_ + (wn * WTN + ((r) - TM) * MI + lrow) * ROWB +       \
+                                 ((((KSUB / 8) * (s4)) ^ sw_row) << 4));           \
 } while (0)
 #define MOE_READ_AT(r) (((r) + 1) * (TM * TN) / (TM + TN) > 0 ? ((r) + 1) * (TM * TN) / (TM + TN) - 1 : 0)
 // The MFMAs of one substep (operands FA, FB) with the fragment reads of
@@ -454,7 +498,7 @@ do {                                                                            
 #define MOE_MFMAS_READ(FA, FB, stage, s4, NA, NB)                                  \
 do {                                                                             \
     _Pragma("unroll") for (int q_ = 0; q_ < TM * TN; ++q_) {                      \
-      acc[q_ / TN][q_ % TN] = MfmaOp<DT>::run(FA[q_ / TN], FB[q_ % TN], acc[q_ / TN][q_ % TN]); \
+      acc[q_ / TN][q_ % TN] = MO::run(FA[q_ / TN], FB[q_ % TN], acc[q_ / TN][q_ % TN]); \
       _Pragma("unroll") for (int r_ = 0; r_ < TM + TN; ++r_)                        \
         if (MOE_READ_AT(r_) == q_) MOE_READ1(stage, s4, r_, NA, NB);                \
       __builtin_amdgcn_sched_barrier(0);                                           \
@@ -519,22 +563,24 @@ do {                                                                            
 
     // Loop invariant at the top of k-step kt: stage kt is visible and its
     // substep 0 is in (xa, xb) (reads possibly in flight); stage kt+1 has
-    // been issued.  Substeps 1..3 are read one substep ahead of their
-    // MFMAs, interleaved with them.  Before the MFMAs of substep 3 the next
-    // stage is made visible; those MFMAs then carry the reads of its
+    // been issued.  Substeps 1 .. NSUB-1 are read one substep ahead of their
+    // MFMAs, interleaved with them.  Before the MFMAs of the last substep the
+    // next stage is made visible; those MFMAs then carry the reads of its
     // substep 0 and the refill of stage kt's buffer (read by every wave by
-    // then) with stage kt+2, one copy per MFMA, so the issue slots overlap
-    // the matrix pipe.  The body is straight-line so the compiler's own LDS
+    // then) with stage kt+2, spread evenly over the MFMAs, so the issue slots
+    // overlap the matrix pipe.  The body is straight-line so the compiler's own LDS
     // wait counts stay exact.
     int kt = 0;
     for (; kt < nk - 2; ++kt) {
       const int st = kt & 1;
-      MOE_MFMAS_READ(xa, xb, st, 1, ya, yb);
-      MOE_PHASE();
-      MOE_MFMAS_READ(ya, yb, st, 2, xa, xb);
-      MOE_PHASE();
-      MOE_MFMAS_READ(xa, xb, st, 3, ya, yb);
-      MOE_PHASE();
+      // substeps 0 .. NSUB-2, alternating the two fragment sets (NSUB is
+      // even, so the last substep's fragments end up in ya, yb)
+#pragma unroll
+      for (int s4 = 0; s4 + 1 < NSUB; ++s4) {
+        if ((s4 & 1) == 0) MOE_MFMAS_READ(xa, xb, st, s4 + 1, ya, yb);
+        else MOE_MFMAS_READ(ya, yb, st, s4 + 1, xa, xb);
+        MOE_PHASE();
+      }
       // prefetch groups issued after stage kt+1's copies: the prologue's two
       // for kt = 0, else the one issued with them (if any)
       MOE_STAGE_READY(kt == 0 ? npf0 : (kt + 3 < nk));
@@ -547,7 +593,7 @@ do {                                                                            
         constexpr int EVERY = MF / BPW > 0 ? MF / BPW : 1;
 #pragma unroll
         for (int q = 0; q < MF; ++q) {
-          acc[q / TN][q % TN] = MfmaOp<DT>::run(ya[q / TN], yb[q % TN], acc[q / TN][q % TN]);
+          acc[q / TN][q % TN] = MO::run(ya[q / TN], yb[q % TN], acc[q / TN][q % TN]);
 #pragma unroll
           for (int r_ = 0; r_ < TM + TN; ++r_)
             if (MOE_READ_AT(r_) == q) MOE_READ1(st ^ 1, 0, r_, xa, xb);
@@ -567,18 +613,19 @@ do {                                                                            
     // Last two k-steps: no refill.
     for (; kt < nk; ++kt) {
       const int st = kt & 1;
-      MOE_READ(st, 1, ya, yb);
-      MOE_PHASE();
-      MOE_MFMAS(xa, xb);
-      MOE_PHASE();
-      MOE_READ(st, 2, xa, xb);
-      MOE_PHASE();
-      MOE_MFMAS(ya, yb);
-      MOE_PHASE();
-      MOE_READ(st, 3, ya, yb);
-      MOE_PHASE();
-      MOE_MFMAS(xa, xb);
-      MOE_PHASE();
+#pragma unroll
+      for (int s4 = 0; s4 + 1 < NSUB; ++s4) {
+        if ((s4 & 1) == 0) {
+          MOE_READ(st, s4 + 1, ya, yb);
+          MOE_PHASE();
+          MOE_MFMAS(xa, xb);
+        } else {
+          MOE_READ(st, s4 + 1, xa, xb);
+          MOE_PHASE();
+          MOE_MFMAS(ya, yb);
+        }
+        MOE_PHASE();
+      }
       if (kt + 1 < nk) {
         MOE_STAGE_READY(kt == 0 ? npf0 : (kt + 3 < nk));
         MOE_READ(st ^ 1, 0, xa, xb);
@@ -600,7 +647,7 @@ do {                                                                            
 #undef MOE_KOFS
 
     // Epilogue (32x32 f32 layout: lane l -> column l % 32, rows
-    // 8*(v/4) + 4*(l/32) + v%4).  One accumulator block (or SwiGLU pair) at a
+    // 8*(v/4) + 4*(l/32) + v%4; 16x16: column l % 16, rows 4*(l/16) + v).  One accumulator block (or SwiGLU pair) at a
     // time; each value is read from the accumulator registers where it is
     // used (acc_read), so the epilogue never holds more than a block of
     // them in vector registers.  The s_nop wait states cover the last MFMAs'
@@ -615,13 +662,13 @@ do {                                                                            
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int v = 0; v < 16; v += 4) {
+          for (int v = 0; v < NV; v += 4) {
             f32x4 q;
             q[0] = acc_read(acc[i][j][v]);
             q[1] = acc_read(acc[i][j][v + 1]);
             q[2] = acc_read(acc[i][j][v + 2]);
             q[3] = acc_read(acc[i][j][v + 3]);
-            *(f32x4*)(mine + (i * TN + j) * 16 + v) = q;
+            *(f32x4*)(mine + (i * TN + j) * NV + v) = q;
           }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -640,8 +687,8 @@ do {                                                                            
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int v = 0; v < 16; v += 4) {
-            const int off = (i * TN + j) * 16 + v;
+          for (int v = 0; v < NV; v += 4) {
+            const int off = (i * TN + j) * NV + v;
             f32x4 tot = *(const f32x4*)(base + off);
             for (int s2 = 1; s2 < ks->parts; ++s2)
               tot += *(const f32x4*)(base + s2 * ks->slot_step + off);
@@ -652,14 +699,14 @@ do {                                                                            
           }
       asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
     }
-    const int rsub = khalf * 4;
+    const int rsub = kgrp * 4;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      int crow[16];
-      bool ok[16];
+      int crow[NV];
+      bool ok[NV];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int grow = ti.r0 + wm * WTM + i * 32 + (v >> 2) * 8 + rsub + (v & 3);
+      for (int v = 0; v < NV; ++v) {
+        const int grow = ti.r0 + wm * WTM + i * MI + (MI == 32 ? (v >> 2) * 8 + (v & 3) : v) + rsub;
         crow[v] = grow - c_sub;
         ok[v] = grow < ti.r1 && !(p.c_local && crow[v] >= p.c_rows);
       }
@@ -668,11 +715,16 @@ do {                                                                            
 #pragma unroll
         for (int jp = 0; jp < TN / 2; ++jp) {
           __builtin_amdgcn_sched_barrier(0);
-          const int col = n0h + (wn * (TN / 2) + jp) * 32 + lrow;
+          // B rows alternate 32 gate and 32 up weight rows: MI = 32 pairs
+          // blocks (2jp, 2jp+1); MI = 16 pairs (g, g+2), g = 4 (jp/2) + jp%2
+          const int jg = MI == 32 ? 2 * jp : 4 * (jp >> 1) + (jp & 1);
+          const int ju = MI == 32 ? jg + 1 : jg + 2;
+          const int col = MI == 32 ? n0h + (wn * (TN / 2) + jp) * 32 + lrow
+                                   : n0h + (wn * (WTN / 64) + (jp >> 1)) * 32 + (jp & 1) * 16 + lrow;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
+          for (int v = 0; v < NV; ++v) {
             if (!ok[v]) continue;
-            const float h = silu_mul(acc_read(acc[i][2 * jp][v]), acc_read(acc[i][2 * jp + 1][v]));
+            const float h = silu_mul(acc_read(acc[i][jg][v]), acc_read(acc[i][ju][v]));
             C[(long long)crow[v] * p.ldc + col] = Act<DT>::store(h);
           }
         }
@@ -680,9 +732,9 @@ do {                                                                            
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           __builtin_amdgcn_sched_barrier(0);
-          const int col = n0 + wn * WTN + j * 32 + lrow;
+          const int col = n0 + wn * WTN + j * MI + lrow;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
+          for (int v = 0; v < NV; ++v) {
             if (!ok[v]) continue;
             float y = acc_read(acc[i][j][v]);
             if (EPI == EPI_F32) {

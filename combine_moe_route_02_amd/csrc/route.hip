@@ -235,26 +235,12 @@ __global__ void __launch_bounds__(256)
 // their partial 16x16 sums are added in wave order through LDS (a fixed
 // order: the result does not depend on timing).
 // Expert rows past E are replaced by zeros and not written.
-template <int DT>
-struct Mfma16 {
-  typedef bf16x8 V;
-  static __device__ __forceinline__ f32x4 run(V a, V b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-template <>
-struct Mfma16<MOE_DTYPE_F16> {
-  typedef f16x8 V;
-  static __device__ __forceinline__ f32x4 run(V a, V b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-  }
-};
 
 template <int DT, int NW, int U>
 __global__ void __launch_bounds__(NW * 64)
     router_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
                        int T, int H, int E, float* __restrict__ logits) {
-  typedef typename Mfma16<DT>::V V;
+  typedef typename MfmaT<DT, 16>::V V;
   __shared__ f32x4 part[NW][64];
   const int lane = lane_id();
   const int wave = (int)threadIdx.x >> 6;
@@ -283,7 +269,7 @@ __global__ void __launch_bounds__(NW * 64)
       const bool in = ks + u < ks1;
       const uint4 av = in ? a[u] : zero;
       const uint4 bv = (in && ev) ? b[u] : zero;
-      acc = Mfma16<DT>::run(__builtin_bit_cast(V, av), __builtin_bit_cast(V, bv), acc);
+      acc = MfmaT<DT, 16>::run(__builtin_bit_cast(V, av), __builtin_bit_cast(V, bv), acc);
     }
   }
   part[wave][lane] = acc;
