@@ -340,6 +340,23 @@ struct DmaTile {
   static constexpr int NACC = TM * TN * NV;  // accumulators per thread
   static constexpr long long SLOT = (long long)NT * NACC;  // floats per split slot
 
+  // Output staging: the tile's outputs (OES bytes each, OCOLS per row) in
+  // the stage buffers, OPITCH bytes per row, 16-byte pieces of row r
+  // swizzled by ochunk(r); OCPR pieces per row, ORPP rows per pass of the
+  // block.
+  static constexpr int OES = EPI == EPI_F32 ? 4 : 2;
+  static constexpr int OCOLS = EPI == EPI_SWIGLU ? BN / 2 : BN;
+  static constexpr int OPITCH = OCOLS * OES;
+  static constexpr int OCPR = OPITCH / 16;
+  static constexpr int ORPP = NT / OCPR;
+  static constexpr int OSPAN = MI * OES / 16;  // pieces one row group of a write covers
+  static constexpr bool EPI_STAGED = BM * OPITCH <= NS * STAGE && NT % OCPR == 0 &&
+                                     BM % ORPP == 0 && OCPR >= (64 / MI) * OSPAN;
+  __device__ static __forceinline__ int ochunk(int r) { return ((r >> 2) & (64 / MI - 1)) * OSPAN; }
+  __device__ static __forceinline__ int obyte(int r, int c) {
+    return r * OPITCH + ((((c * OES) >> 4) ^ ochunk(r)) << 4) + ((c * OES) & 15);
+  }
+
   __device__ static __forceinline__ void run(const GemmArgs& p, const TileInfo& ti, int nt,
                                              char* smem, const int32_t* a_gather,
                                              const KSplit* ks = nullptr) {
@@ -700,6 +717,78 @@ do {                                                                            
       asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
     }
     const int rsub = kgrp * 4;
+    if (EPI_STAGED && ((uintptr_t)p.C & 15) == 0 && ((long long)p.ldc * OES) % 16 == 0) {
+      // Staged output: every wave is done with the stage buffers, which now
+      // take the finished tile (activation applied, in the output type);
+      // then each thread stores whole 16-byte pieces of output rows.  One
+      // 16-byte store instead of 8 (16-bit) or 4 (f32) single-value stores,
+      // each covering a full row segment, cuts the store instructions and the
+      // partial-line writes they caused.  Chunk swizzle (see ochunk): the 64
+      // lanes of one staging write cover 64 / MI rows 4 apart, moved to
+      // distinct banks.
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if (EPI == EPI_SWIGLU) {
+#pragma unroll
+          for (int jp = 0; jp < TN / 2; ++jp) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int jg = MI == 32 ? 2 * jp : 4 * (jp >> 1) + (jp & 1);
+            const int ju = MI == 32 ? jg + 1 : jg + 2;
+            const int ocol = MI == 32 ? (wn * (TN / 2) + jp) * 32 + lrow
+                                      : (wn * (WTN / 64) + (jp >> 1)) * 32 + (jp & 1) * 16 + lrow;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+              const int orow = wm * WTM + i * MI + (MI == 32 ? (v >> 2) * 8 + (v & 3) : v) + rsub;
+              const float h = silu_mul(acc_read(acc[i][jg][v]), acc_read(acc[i][ju][v]));
+              *(uint16_t*)(smem + obyte(orow, ocol)) = Act<DT>::store(h);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int ocol = wn * WTN + j * MI + lrow;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+              const int orow = wm * WTM + i * MI + (MI == 32 ? (v >> 2) * 8 + (v & 3) : v) + rsub;
+              float y = acc_read(acc[i][j][v]);
+              if (EPI == EPI_F32) {
+                *(float*)(smem + obyte(orow, ocol)) = y;
+              } else {
+                if (EPI == EPI_GELU) y = gelu_erf16(y);
+                *(uint16_t*)(smem + obyte(orow, ocol)) = Act<DT>::store(y);
+                if (EPI == EPI_GELU) __builtin_amdgcn_sched_barrier(0);
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();
+      // Thread t stores 16-byte piece t % OCPR of rows t / OCPR + k * ORPP.
+      const int c16 = tid % OCPR;
+      const int nrows = ti.r1 - ti.r0;
+      char* cbase = (char*)p.C + (long long)(EPI == EPI_SWIGLU ? n0h : n0) * OES + c16 * 16;
+      constexpr int NQ = BM / ORPP;
+      constexpr int QB = NQ < 4 ? NQ : 4;  // pieces in flight per thread
+#pragma unroll 1
+      for (int q0 = 0; q0 < NQ; q0 += QB) {
+        uint4 val[QB];
+#pragma unroll
+        for (int u = 0; u < QB; ++u) {
+          const int rr = tid / OCPR + (q0 + u) * ORPP;
+          val[u] = *(const uint4*)(smem + rr * OPITCH + ((c16 ^ ochunk(rr)) << 4));
+        }
+#pragma unroll
+        for (int u = 0; u < QB; ++u) {
+          const int rr = tid / OCPR + (q0 + u) * ORPP;
+          const int crow = ti.r0 + rr - c_sub;
+          if (rr < nrows && !(p.c_local && crow >= p.c_rows))
+            *(uint4*)(cbase + (long long)crow * p.ldc * OES) = val[u];
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       int crow[NV];
