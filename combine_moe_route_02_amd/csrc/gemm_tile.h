@@ -233,6 +233,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
+// Wait until at most BASE + n * STEP vector memory operations are in flight
+// (n <= N, wave-uniform; the count must be an immediate).
+template <int BASE, int STEP, int N>
+__device__ __forceinline__ void wait_vmcnt_groups(int n) {
+  if constexpr (N > 0) {
+    if (n >= N) wait_vmcnt<BASE + N * STEP>();
+    else wait_vmcnt_groups<BASE, STEP, N - 1>(n);
+  } else {
+    wait_vmcnt<BASE>();
+  }
+}
+
 // Workgroup barrier for LDS hand-off that does not drain outstanding loads.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x7 << 4) | (0x0 << 8) | ((0x3F >> 4) << 14));
@@ -327,14 +339,18 @@ struct DmaTile {
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int A_BLK = BM / 8, B_BLK = BN / 8;  // 1 KB blocks of 8 rows
   static constexpr int BPW = (A_BLK + B_BLK) / NW;       // DMA blocks per wave
-  static constexpr int NPA = (BM + 64 * NW - 1) / (64 * NW);  // A prefetches per wave
-  static constexpr int NPF = NPA + (BN + 64 * NW - 1) / (64 * NW);  // prefetches per wave
+  // L2 prefetch: weight (B) rows PFD k-steps ahead, one dword per 128-byte
+  // line.  Activation rows are not prefetched: a band's workgroups share
+  // them and keep them in L2, while prefetching them too evicts weight lines
+  // before their copies (GEMM-1 and GEMM-2 5-15% slower measured with both).
+  static constexpr int PFD = 4;
+  static constexpr int NPF = (BN + 64 * NW - 1) / (64 * NW);  // prefetches per wave and k-step
   static constexpr int PF_OFS = NS * STAGE;                         // scratch slots
   static constexpr int SMEM = NS * STAGE + NW * 256;
   static_assert(A_BLK % NW == 0 && B_BLK % NW == 0, "blocks per wave");
   static_assert(TM >= 1 && TN >= 1, "tile");
   static_assert(EPI != EPI_SWIGLU || (TN % (MI == 32 ? 2 : 4)) == 0, "swiglu pairs");
-  static_assert(BPW + 2 * NPF < 64, "vmcnt range");
+  static_assert(PFD >= 3 && BPW + (PFD - 2) * NPF < 64, "vmcnt range");
   static_assert(MI == 32 || MI == 16, "MFMA shape");
 
   static constexpr int NACC = TM * TN * NV;  // accumulators per thread
@@ -426,36 +442,21 @@ struct DmaTile {
       }
     }
 
-    // L2 prefetch rows: prefetch i < NPA covers A rows (i * NW + wave) * 64 +
-    // lane, the others B rows likewise (past the end: the last row again).
+    // L2 prefetch rows: prefetch i covers B rows (i * NW + wave) * 64 + lane
+    // (past the end: the last row again).
     uint32_t pfoff[NPF];
 #pragma unroll
     for (int i = 0; i < NPF; ++i) {
-      if (i < NPA) {
-        int r = (i * NW + wave) * 64 + lane;
-        r = r < BM ? r : BM - 1;
-        int grow = ti.r0 + r;
-        grow = grow < ti.r1 ? grow : ti.r1 - 1;
-        int arow;
-        if (a_gather) {
-          arow = a_gather[grow];
-        } else {
-          arow = grow - a_sub;
-          if (p.a_local && arow >= p.a_rows) arow = p.a_rows - 1;
-        }
-        pfoff[i] = (uint32_t)(arow - base_row) * (uint32_t)(p.lda * 2);
+      int row = (i * NW + wave) * 64 + lane;
+      row = row < BN ? row : BN - 1;
+      int n;
+      if (EPI == EPI_SWIGLU) {
+        const int gi = row >> 5;
+        n = ((gi & 1) ? p.I : 0) + n0h + (gi >> 1) * 32 + (row & 31);
       } else {
-        int row = ((i - NPA) * NW + wave) * 64 + lane;
-        row = row < BN ? row : BN - 1;
-        int n;
-        if (EPI == EPI_SWIGLU) {
-          const int gi = row >> 5;
-          n = ((gi & 1) ? p.I : 0) + n0h + (gi >> 1) * 32 + (row & 31);
-        } else {
-          n = n0 + row;
-        }
-        pfoff[i] = (uint32_t)n * (uint32_t)(p.ldb * 2);
+        n = n0 + row;
       }
+      pfoff[i] = (uint32_t)n * (uint32_t)(p.ldb * 2);
     }
 
     typename MO::Acc acc[TM][TN];
@@ -543,17 +544,11 @@ do {                                                                            
 do {                                                                             \
     const uint32_t pdst_ = lds0 + PF_OFS + wave * 256;                             \
     _Pragma("unroll") for (int i = 0; i < NPF; ++i)                                \
-      prefetch4((i < NPA ? a_tile : b_tile) + MOE_KOFS(st), pfoff[i], pdst_);      \
+      prefetch4(b_tile + MOE_KOFS(st), pfoff[i], pdst_);                           \
 } while (0)
 // Wait until at most n_pf prefetch groups (issued after the stage's copies)
 // are in flight.
-#define MOE_WAIT_STAGE(n_pf)                                                       \
-do {                                                                             \
-    const int np_ = (n_pf);                                                        \
-    if (np_ >= 2) wait_vmcnt<2 * NPF>();                                           \
-    else if (np_ == 1) wait_vmcnt<NPF>();                                          \
-    else wait_vmcnt<0>();                                                          \
-} while (0)
+#define MOE_WAIT_STAGE(n_pf) wait_vmcnt_groups<0, NPF, PFD - 2>(n_pf)
 // sched_barrier(0) keeps each phase's LDS reads ahead of the MFMAs that
 // overlap them (the scheduler would otherwise sink each read to its use).
 #define MOE_PHASE() __builtin_amdgcn_sched_barrier(0)
@@ -563,16 +558,14 @@ do {                                                                            
     lds_barrier();
     MOE_ISSUE(0);
     if (nk > 1) MOE_ISSUE(1);
-    if (nk > 2) MOE_PREFETCH(2);
-    if (nk > 3) MOE_PREFETCH(3);
-    // stage 0 landed; stage 1 and the prefetches may be in flight
-    const int npf0 = nk > 3 ? 2 : (nk > 2 ? 1 : 0);
-    {
-      if (nk <= 1) wait_vmcnt<0>();
-      else if (npf0 == 0) wait_vmcnt<BPW>();
-      else if (npf0 == 1) wait_vmcnt<BPW + NPF>();
-      else wait_vmcnt<BPW + 2 * NPF>();
-    }
+#pragma unroll
+    for (int s_ = 2; s_ < PFD; ++s_)
+      if (s_ < nk) MOE_PREFETCH(s_);
+    // stage 0 landed; stage 1 and the npf0 prefetch groups issued after it
+    // may be in flight
+    const int npf0 = nk > 2 ? (nk < PFD ? nk : PFD) - 2 : 0;
+    if (nk <= 1) wait_vmcnt<0>();
+    else wait_vmcnt_groups<BPW, NPF, PFD - 2>(npf0);
     __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x7 << 4) | ((0x3F >> 4) << 14));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -598,9 +591,9 @@ do {                                                                            
         else MOE_MFMAS_READ(ya, yb, st, s4 + 1, xa, xb);
         MOE_PHASE();
       }
-      // prefetch groups issued after stage kt+1's copies: the prologue's two
-      // for kt = 0, else the one issued with them (if any)
-      MOE_STAGE_READY(kt == 0 ? npf0 : (kt + 3 < nk));
+      // prefetch groups issued after stage kt+1's copies: the prologue's
+      // npf0 for kt = 0, else the one issued with them (if any)
+      MOE_STAGE_READY(kt == 0 ? npf0 : (kt + PFD - 1 < nk));
       {
         const uint32_t dst_ = lds0 + st * STAGE;
         const int kofs_ = MOE_KOFS(kt + 2);
@@ -624,7 +617,7 @@ do {                                                                            
           MOE_PHASE();
         }
       }
-      if (kt + 4 < nk) MOE_PREFETCH(kt + 4);
+      if (kt + PFD < nk) MOE_PREFETCH(kt + PFD);
       MOE_PHASE();
     }
     // Last two k-steps: no refill.
@@ -644,7 +637,7 @@ do {                                                                            
         MOE_PHASE();
       }
       if (kt + 1 < nk) {
-        MOE_STAGE_READY(kt == 0 ? npf0 : (kt + 3 < nk));
+        MOE_STAGE_READY(kt == 0 ? npf0 : (kt + PFD - 1 < nk));
         MOE_READ(st ^ 1, 0, xa, xb);
         MOE_PHASE();
       }
