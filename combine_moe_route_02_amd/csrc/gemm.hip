@@ -521,20 +521,30 @@ __global__ void __launch_bounds__(WM * WN * 64)
   const int len = (int)((long long)total * (xcd + 1) / 8) - lo;
   const int full = len / per;
   const int rem = len - full * per;
-  for (int r = 0; r < full; ++r) {
-    int mt, nt;
-    const TileInfo ti = band_tile<BM>(p, s_pre, lo + r * per + idx, p.n_tiles, p.gm, mt, nt);
-    Tile::run(p, ti, nt, smem, nullptr);
-  }
-  if (rem == 0) return;
   const int nk_all = p.K / Tile::BK;
   int S = 1;
-  if (p.split_ws != nullptr && 2 * rem <= per) {
+  if (rem > 0 && p.split_ws != nullptr && 2 * rem <= per) {
     S = per / rem;
     if (S > 8) S = 8;
     if (S > nk_all / 4) S = nk_all / 4;  // at least 4 k-steps per part
     if (S < 1) S = 1;
   }
+  for (int r = 0; r < full; ++r) {
+    int mt, nt;
+    const TileInfo ti = band_tile<BM>(p, s_pre, lo + r * per + idx, p.n_tiles, p.gm, mt, nt);
+    // the next full-K tile of this workgroup, if any (its weight lines are
+    // prefetched during this tile's epilogue)
+    int nx = -1;
+    if (r + 1 < full) nx = lo + (r + 1) * per + idx;
+    else if (rem > 0 && S == 1 && idx < rem) nx = lo + full * per + idx;
+    int nx_g = -1, nx_nt = 0;
+    if (nx >= 0) {
+      int mt2;
+      nx_g = band_tile<BM>(p, s_pre, nx, p.n_tiles, p.gm, mt2, nx_nt).g;
+    }
+    Tile::run(p, ti, nt, smem, nullptr, nullptr, nx_g, nx_nt);
+  }
+  if (rem == 0) return;
   if (S == 1) {
     if (idx < rem) {
       int mt, nt;

@@ -373,9 +373,14 @@ struct DmaTile {
     return r * OPITCH + ((((c * OES) >> 4) ^ ochunk(r)) << 4) + ((c * OES) & 15);
   }
 
+  // nxt_g >= 0: this workgroup's next tile is the full-K tile of group
+  // nxt_g, n-tile nxt_nt; the weight lines of its first PFD k-steps are
+  // prefetched into L2 before this tile's epilogue, so that its first
+  // copies do not wait on HBM.
   __device__ static __forceinline__ void run(const GemmArgs& p, const TileInfo& ti, int nt,
                                              char* smem, const int32_t* a_gather,
-                                             const KSplit* ks = nullptr) {
+                                             const KSplit* ks = nullptr, int nxt_g = -1,
+                                             int nxt_nt = 0) {
     typedef typename MO::V V;
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63;
@@ -655,6 +660,32 @@ do {                                                                            
 #undef MOE_PREFETCH
 #undef MOE_WAIT_STAGE
 #undef MOE_KOFS
+
+    if (nxt_g >= 0) {
+      const char* b2 = uniform_ptr((const char*)p.B + (long long)nxt_g * p.strideB * 2);
+      const int nk2 = p.K / BK;
+      const int skew2 = MOE_SKEW(nxt_nt, nk2);
+      const uint32_t pdst = lds0 + PF_OFS + wave * 256;
+#pragma unroll
+      for (int i = 0; i < NPF; ++i) {
+        int row = (i * NW + wave) * 64 + lane;
+        row = row < BN ? row : BN - 1;
+        int n;
+        if (EPI == EPI_SWIGLU) {
+          const int gi = row >> 5;
+          n = ((gi & 1) ? p.I : 0) + nxt_nt * (BN / 2) + (gi >> 1) * 32 + (row & 31);
+        } else {
+          n = nxt_nt * BN + row;
+        }
+        const uint32_t off = (uint32_t)n * (uint32_t)(p.ldb * 2);
+#pragma unroll
+        for (int s_ = 0; s_ < PFD; ++s_)
+          if (s_ < nk2) {
+            const int kk = s_ + skew2 < nk2 ? s_ + skew2 : s_ + skew2 - nk2;
+            prefetch4(b2 + kk * ROWB, off, pdst);
+          }
+      }
+    }
 
     // Epilogue (32x32 f32 layout: lane l -> column l % 32, rows
     // 8*(v/4) + 4*(l/32) + v%4; 16x16: column l % 16, rows 4*(l/16) + v).  One accumulator block (or SwiGLU pair) at a
