@@ -39,6 +39,11 @@ bool act_ok(int dt) {
 int elem_bytes(int dt) { return dt == MOE_DTYPE_F32 ? 4 : 2; }
 bool pairs_fit(long long T, long long k) { return T * k < (1ll << 31); }
 
+// Row buffers are copied in 16-byte pieces (and staged to LDS by DMA), so
+// their bases must be 16-byte aligned; a null pointer passes here and is
+// rejected (or allowed) by the caller's own checks.
+bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 // Weight format accepted for a given activation format.
 bool weights_ok(int act_dtype, int w_dtype) {
   if (w_dtype == act_dtype) return true;
@@ -62,6 +67,7 @@ int moe_route(const void* x, const void* w_router, int act_dtype, const float* b
   if (T == 0) return MOE_OK;
   if (!logits || !topk_idx || !topk_w) return MOE_ERR_ARG;
   if (w_router && (!x || H < 1 || H % 8)) return MOE_ERR_ARG;
+  if (w_router && (!al16(x) || !al16(w_router))) return MOE_ERR_ARG;
   return route_impl(x, w_router, act_dtype, bias, T, H, E, k, gate, renorm,
                     inv_temperature, min_prob, logits, topk_idx, topk_w, stream);
 }
@@ -79,6 +85,7 @@ int moe_dispatch(const void* x, int act_dtype, const int32_t* topk_idx, int T, i
   if (!counts || !offsets) return MOE_ERR_ARG;
   if (T > 0 && (!x || !topk_idx || !slot_of || !row_token)) return MOE_ERR_ARG;
   if (T > 0 && e_end > e_begin && !x_perm) return MOE_ERR_ARG;
+  if (!al16(x) || !al16(x_perm)) return MOE_ERR_ARG;
   if (!ws || ws_bytes < dispatch_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
   return dispatch_impl(x, act_dtype, topk_idx, T, H, E, k, e_begin, e_end, counts,
                        offsets, slot_of, row_token, x_perm, nullptr, ws, stream);
@@ -98,6 +105,7 @@ int moe_dispatch_fp8(const void* x, int act_dtype, const int32_t* topk_idx, int 
   if (!counts || !offsets) return MOE_ERR_ARG;
   if (T > 0 && (!x || !topk_idx || !slot_of || !row_token)) return MOE_ERR_ARG;
   if (T > 0 && e_end > e_begin && (!x_perm_q || !x_scale)) return MOE_ERR_ARG;
+  if (!al16(x) || !al16(x_perm_q)) return MOE_ERR_ARG;
   if (!ws || ws_bytes < dispatch_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
   return dispatch_impl(x, act_dtype, topk_idx, T, H, E, k, e_begin, e_end, counts,
                        offsets, slot_of, row_token, x_perm_q,
@@ -114,6 +122,7 @@ int moe_expert_ffn_up(const void* x_perm, const int32_t* offsets, int act_dtype,
     return MOE_ERR_ARG;
   if (e_end == e_begin || max_rows == 0) return MOE_OK;
   if (!x_perm || !offsets || !w13 || !h_ws) return MOE_ERR_ARG;
+  if (!al16(x_perm) || !al16(w13) || !al16(h_ws)) return MOE_ERR_ARG;
   if (w_dtype == MOE_DTYPE_FP8_E4M3 && !w13_scale) return MOE_ERR_ARG;
   if (ws && ws_bytes < ffn_ws_bytes()) return MOE_ERR_WORKSPACE;
   const int Nb = act == MOE_ACT_SWIGLU ? 2 * I : I;
@@ -151,6 +160,7 @@ int moe_expert_ffn_up_fp8(const void* x_perm_q, const float* x_scale,
     return MOE_ERR_ARG;
   if (e_end == e_begin || max_rows == 0) return MOE_OK;
   if (!x_perm_q || !x_scale || !offsets || !w13 || !w13_scale || !h_ws) return MOE_ERR_ARG;
+  if (!al16(x_perm_q) || !al16(w13) || !al16(h_ws)) return MOE_ERR_ARG;
   const int Nb = act == MOE_ACT_SWIGLU ? 2 * I : I;
   if (H % 128 || I % 128 || Nb % 256) return MOE_ERR_UNSUPPORTED;
   GemmArgs a{};
@@ -186,6 +196,7 @@ int moe_expert_ffn_down(const int32_t* offsets, int act_dtype, int H, int I, int
     return MOE_ERR_ARG;
   if (e_end == e_begin || max_rows == 0) return MOE_OK;
   if (!offsets || !w2 || !h_ws || !y_perm) return MOE_ERR_ARG;
+  if (!al16(w2) || !al16(h_ws) || !al16(y_perm)) return MOE_ERR_ARG;
   if (w_dtype == MOE_DTYPE_FP8_E4M3 && !w2_scale) return MOE_ERR_ARG;
   if (ws && ws_bytes < ffn_ws_bytes()) return MOE_ERR_WORKSPACE;
   GemmArgs a{};
@@ -219,6 +230,8 @@ int moe_expert_ffn(const void* x_perm, const int32_t* offsets, int act_dtype, in
   if (!act_ok(act_dtype) || !weights_ok(act_dtype, w_dtype)) return MOE_ERR_UNSUPPORTED;
   if (act != MOE_ACT_SWIGLU && act != MOE_ACT_GELU) return MOE_ERR_ARG;
   if (e_end > e_begin && max_rows > 0 && (!y_perm || !w2)) return MOE_ERR_ARG;
+  if (!al16(x_perm) || !al16(w13) || !al16(w2) || !al16(h_ws) || !al16(y_perm))
+    return MOE_ERR_ARG;
   if (ws && ws_bytes < ffn_ws_bytes()) return MOE_ERR_WORKSPACE;
   // Shape checks of both halves happen before either launches.
   const int Nb = act == MOE_ACT_SWIGLU ? 2 * I : I;
@@ -262,6 +275,7 @@ int moe_combine(const void* y_perm, const int32_t* slot_of, const float* topk_w,
   if ((H * elem_bytes(act_dtype)) % 16) return MOE_ERR_ARG;
   if (T == 0) return MOE_OK;
   if (!y_perm || !slot_of || !topk_w || !out) return MOE_ERR_ARG;
+  if (!al16(y_perm) || !al16(out)) return MOE_ERR_ARG;
   return combine_impl(y_perm, slot_of, topk_w, act_dtype, T, H, k, out, stream);
 }
 
@@ -281,6 +295,8 @@ int moe_layer_fused(const void* x, const int32_t* offsets, const int32_t* slot_o
   if (!x || !offsets || !slot_of || !row_token || !topk_w || !y_perm || !out)
     return MOE_ERR_ARG;
   if (e_end > e_begin && (!w13 || !w2 || !h_ws)) return MOE_ERR_ARG;
+  if (!al16(x) || !al16(w13) || !al16(w2) || !al16(h_ws) || !al16(y_perm) || !al16(out))
+    return MOE_ERR_ARG;
   if (!ws || ws_bytes < fused_ws_bytes(T, H, E, k, I)) return MOE_ERR_WORKSPACE;
   return fused_impl(x, offsets, slot_of, row_token, topk_w, act_dtype, T, H, E, k, I,
                     e_begin, e_end, act, w13, w2, h_ws, y_perm, out, ws, ws_bytes, stream);

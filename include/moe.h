@@ -26,8 +26,9 @@
  *    launch failed (hipGetLastError).  Faults inside kernels are not reported
  *    synchronously.
  *  - Index type is int32; calls with T*k >= 2^31 are rejected.
- *  - Rows are contiguous with leading dimension H (or I); x, x_perm, y_perm,
- *    out and the weights must be 16-byte aligned.  Logits must be finite.
+ *  - Rows are contiguous with leading dimension H (or I); x, x_perm (and
+ *    x_perm_q), h_ws, y_perm, out and the weights must be 16-byte aligned
+ *    (checked: MOE_ERR_ARG).  Logits must be finite.
  *  - act_dtype selects the activation format: MOE_DTYPE_F32, MOE_DTYPE_F16
  *    or MOE_DTYPE_BF16.  Expert weights use act_dtype, or MOE_DTYPE_FP8_E4M3
  *    (OCP E4M3FN codes with one float32 scale per 128x128 tile) with bf16

@@ -187,3 +187,46 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(L, "LIB_PATH", "/nonexistent/libmoe.so")
     with pytest.raises(ImportError):
         L.lib()
+
+
+ODD = ctypes.c_void_p(0x1002)   # a row buffer off its 16-byte alignment
+
+
+def test_misaligned_row_buffers_are_rejected():
+    """Row buffers are copied in 16-byte pieces: a base off 16-byte alignment
+    is refused on the host (MOE_ERR_ARG) before anything is launched."""
+    lib = L.lib()
+    assert _route(x=ODD) == L.MOE_ERR_ARG
+    assert _route(w=ODD) == L.MOE_ERR_ARG
+    assert _dispatch(x=ODD) == L.MOE_ERR_ARG
+    assert _dispatch(xp=ODD) == L.MOE_ERR_ARG
+
+    def up(x=FAKE, w=FAKE, h=FAKE):
+        return lib.moe_expert_ffn_up(x, FAKE, L.DTYPE_BF16, 256, 128, 0, 8, 64, 0, w, None,
+                                     L.DTYPE_BF16, h, None, 0, None)
+    assert up(x=ODD) == up(w=ODD) == up(h=ODD) == L.MOE_ERR_ARG
+
+    def down(w=FAKE, h=FAKE, y=FAKE):
+        return lib.moe_expert_ffn_down(FAKE, L.DTYPE_BF16, 256, 128, 0, 8, 64, w, None,
+                                       L.DTYPE_BF16, h, y, None, 0, None)
+    assert down(w=ODD) == down(h=ODD) == down(y=ODD) == L.MOE_ERR_ARG
+
+    def both(x=FAKE, w13=FAKE, w2=FAKE, h=FAKE, y=FAKE):
+        return lib.moe_expert_ffn(x, FAKE, L.DTYPE_BF16, 256, 128, 0, 8, 64, 0, w13, None,
+                                  w2, None, L.DTYPE_BF16, h, y, None, 0, None)
+    for kw in ("x", "w13", "w2", "h", "y"):
+        assert both(**{kw: ODD}) == L.MOE_ERR_ARG, kw
+
+    assert lib.moe_combine(ODD, FAKE, FAKE, L.DTYPE_BF16, 4, 64, 1, FAKE, None) == L.MOE_ERR_ARG
+    assert lib.moe_combine(FAKE, FAKE, FAKE, L.DTYPE_BF16, 4, 64, 1, ODD, None) == L.MOE_ERR_ARG
+
+    u = lib.moe_expert_ffn_up_fp8
+    assert u(ODD, FAKE, FAKE, 256, 128, 0, 8, 64, 0, FAKE, FAKE, FAKE, None) == L.MOE_ERR_ARG
+    assert u(FAKE, FAKE, FAKE, 256, 128, 0, 8, 64, 0, ODD, FAKE, FAKE, None) == L.MOE_ERR_ARG
+    assert u(FAKE, FAKE, FAKE, 256, 128, 0, 8, 64, 0, FAKE, FAKE, ODD, None) == L.MOE_ERR_ARG
+
+    def fused(x=FAKE, w13=FAKE, w2=FAKE, h=FAKE, y=FAKE, out=FAKE):
+        return lib.moe_layer_fused(x, FAKE, FAKE, FAKE, FAKE, L.DTYPE_BF16, 4, 256, 8, 2, 128,
+                                   0, 8, 0, w13, w2, h, y, out, FAKE, 1 << 30, None)
+    for kw in ("x", "w13", "w2", "h", "y", "out"):
+        assert fused(**{kw: ODD}) == L.MOE_ERR_ARG, kw
