@@ -106,6 +106,8 @@ ROUTER_SHAPES = [
     small("r_valu_h200", 20, 200, 8, 2, 64, seed_off=73),
     small("r_staged_e256_t1025", 1025, 128, 256, 8, 64, gate=SIGMOID, seed_off=74),
     small("r_staged_e512_f16", 1090, 256, 512, 4, 64, act_dtype=F16, seed_off=75),
+    # E a multiple of 128 but not 256: the grouped GEMM's 64x128 float32 tile
+    small("r_gemm_e384_t1030", 1030, 256, 384, 8, 64, gate=SIGMOID, seed_off=76),
 ]
 
 
@@ -126,6 +128,30 @@ def test_router_projection_paths(cfg):
     idx, w = route(cfg, logits, st["bias"])
     assert np.array_equal(lay.topk_idx.cpu().numpy(), idx)
     assert rel_l2(lay.topk_w.cpu().numpy(), w) <= TOL_F32
+
+
+def test_router_logits_off_alignment():
+    """Logits written to a buffer 4 bytes off 16-byte alignment take the GEMM
+    tile's per-value store path instead of its 16-byte row stores: the same
+    logits, bit for bit, and the same top-k."""
+    from combine_moe_route_02_amd import MoELayer, _lib as L
+    cfg = ROUTER_SHAPES[-1]
+    inp = to_device(make_inputs(cfg, "cpu", with_weights=False))
+    say(f"[gpu] route off alignment {cfg.name} T={cfg.T} H={cfg.H} E={cfg.E}")
+    lay = MoELayer(spec(cfg), "cuda")
+    lay.route(inp["x"], inp["w_router"], inp["bias"])
+    buf = torch.empty(cfg.T * cfg.E + 4, dtype=torch.float32, device="cuda")
+    odd = buf[1:1 + cfg.T * cfg.E].view(cfg.T, cfg.E)
+    assert odd.data_ptr() % 16 != 0
+    idx = torch.empty_like(lay.topk_idx)
+    w = torch.empty_like(lay.topk_w)
+    s = lay.spec
+    from combine_moe_route_02_amd.layer import GATES
+    L.moe_route(inp["x"], inp["w_router"], inp["bias"], s.k, GATES[s.gate], s.renorm,
+                s.inv_temperature, odd, idx, w, min_prob=s.min_prob)
+    torch.cuda.synchronize()
+    assert torch.equal(odd, lay.logits)
+    assert torch.equal(idx, lay.topk_idx) and torch.equal(w, lay.topk_w)
 
 
 @pytest.mark.parametrize("cfg", GRID, ids=[c.name for c in GRID])
