@@ -207,9 +207,9 @@ __device__ __forceinline__ float gelu_erf16(float a) {
 // Stage layout: rows of 128 bytes (64 values, one full cache line of a
 // K-contiguous row); 16-byte chunk kc of row r sits at chunk kc ^ dma_swz(r),
 // so the 16 or 32 rows an MFMA operand read touches (same logical chunk)
-// spread over all bank groups.  One wave instruction fills one 1 KB block (8 rows):
-// lane p writes row p/8, physical chunk p%8, and fetches the logical chunk
-// that belongs there.  Whole 128-byte lines per row matter: the same bytes
+// spread over all bank groups.  One wave instruction fills one 1 KB block
+// (8 rows): lane p writes row p/8, physical chunk p%8, and fetches the
+// logical chunk that belongs there.  Whole 128-byte lines per row matter: the same bytes
 // fetched as 64-byte halves of twice as many lines take twice as many L2
 // requests, and the request rate, not the byte rate, bounds a CU's copies
 // when every k-step touches hundreds of rows.  The hardware performs the LDS
@@ -688,10 +688,10 @@ do {                                                                            
     }
 
     // Epilogue (32x32 f32 layout: lane l -> column l % 32, rows
-    // 8*(v/4) + 4*(l/32) + v%4; 16x16: column l % 16, rows 4*(l/16) + v).  One accumulator block (or SwiGLU pair) at a
-    // time; each value is read from the accumulator registers where it is
-    // used (acc_read), so the epilogue never holds more than a block of
-    // them in vector registers.  The s_nop wait states cover the last MFMAs'
+    // 8*(v/4) + 4*(l/32) + v%4; 16x16: column l % 16, rows 4*(l/16) + v).
+    // One accumulator block (or SwiGLU pair) at a time; each value is read
+    // from the accumulator registers where it is used (acc_read), so the
+    // epilogue never holds more than a block of them in vector registers.  The s_nop wait states cover the last MFMAs'
     // results before the first read.
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     if (ks && ks->parts > 1) {
