@@ -4,13 +4,20 @@ One step = route -> dispatch -> expert FFN (GEMM-1 + SwiGLU, GEMM-2) ->
 combine over one batch of synthetic tokens, every step through the C ABI of
 libmoe.so on one HIP stream, inputs already resident in HBM.
 
-    python bench.py [--steps K] [--warmup W] [--config c2] [--gpus 1]
-                    [--fused] [--temperature T] [--min-prob P] [--fp8-dispatch]
+    python bench.py [--steps K] [--warmup W] [--config c4] [--gpus 1]
+                    [--fused] [--graph on|off|auto] [--flush on|off|auto]
+                    [--temperature T] [--min-prob P] [--fp8-dispatch]
+
+Defaults: the DeepSeek-V3-like EP share (c4, the largest single-GPU layer),
+10 warm-up steps, then 50 timed steps, each bracketed by its own HIP events;
+the line reports their median.  The decode layer (c5) is timed as replays of
+one captured hipGraph, and the small layers (c1, c5) overwrite a 512 MiB
+buffer between steps so that their inputs come from HBM, not the MALL.
 
 Prints one JSON line: whole-layer tokens/s, plus the dominant kernel's
 roofline (GEMM-1, timed live with HIP events on the launch stream), the
 dispatch+combine HBM rate and grouped-GEMM MFMA utilisation, and the CPU
-oracle timed on a bounded sample of the same workload.
+oracle timed per stage on a bounded sample of the same workload.
 """
 
 import argparse
@@ -44,9 +51,10 @@ DT_NAME = {"f32": "f32", "f16": "f16", "bf16": "bf16"}
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD))
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c4", choices=sorted(WORKLOAD),
+                    help="workload (default c4, the largest single-GPU layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -70,9 +78,15 @@ def parse():
     ap.add_argument("--microbatch", type=int, default=0, metavar="N",
                     help="run the layer as N token chunks on two streams (data movement "
                          "of one chunk overlapping another's expert GEMMs)")
-    ap.add_argument("--graph", choices=["on", "off"], default="off",
+    ap.add_argument("--graph", choices=["on", "off", "auto"], default="auto",
                     help="time replays of the whole step captured in one hipGraph "
-                         "(per-stage times then come from one graph per stage)")
+                         "(per-stage times then come from one graph per stage); "
+                         "auto: on for the decode layer c5, whose workload is one "
+                         "captured graph")
+    ap.add_argument("--flush", choices=["on", "off", "auto"], default="auto",
+                    help="overwrite a 512 MiB buffer between timed steps (outside each "
+                         "step's events) so that inputs do not stay in the 256 MiB "
+                         "MALL; auto: on for the small layers c1 and c5")
     ap.add_argument("--fp8-dispatch", action="store_true",
                     help="send the dispatched rows as E4M3 codes with a per-row scale "
                          "into an fp8 x fp8 GEMM-1 (fp8-weight workloads)")
@@ -242,6 +256,11 @@ def main():
         lay.ffn_down(w2, s2)
         lay.combine()
 
+    use_graph = args.graph == "on" or (args.graph == "auto" and cfg.name == "c5"
+                                       and NB <= 1 and not args.fused and R == 0)
+    flush = args.flush == "on" or (args.flush == "auto" and cfg.name in ("c1", "c5"))
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if flush else None
+
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -251,7 +270,6 @@ def main():
         b.copy_(a)      # reads n bytes, writes n bytes
         torch.cuda.synchronize()
         del a, b
-    use_graph = args.graph == "on"
     if use_graph and (NB > 1 or args.fused):
         sys.exit("--graph captures the unfused single-stream step")
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -277,8 +295,13 @@ def main():
     torch.cuda.synchronize()
 
     # -- timed region: exactly K steps ------------------------------------
+    # Each step is bracketed by its own pair of events on the launch stream;
+    # ms_per_step is their median.  With the MALL flush on, the flush runs
+    # between a step's end event and the next step's start event.
     K = args.steps
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(K)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -286,14 +309,20 @@ def main():
     wall0 = time.perf_counter()
     t0.record(stream)
     for i in range(K):
+        if flush_buf is not None:
+            flush_buf.fill_(i & 0xff)
+        sev[i][0].record(stream)
         if graph is not None:
             graph.replay()
         else:
             step(kev[i], i)
+        sev[i][1].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_per_step = t0.elapsed_time(t1) / K
+    step_ms = np.array([a.elapsed_time(b) for a, b in sev])
+    ms_per_step = float(np.median(step_ms))
+    bracket_ms = t0.elapsed_time(t1) / K
     if graph is not None:
         # GEMM-1 launches on the same stream, eager, between events (each
         # launch is long against the host's launch overhead)
@@ -303,11 +332,12 @@ def main():
             b.record(stream)
         torch.cuda.synchronize()
     if NB > 1:   # GEMM-1 launches of every chunk, on the compute stream
-        gemm1_ms = float(np.mean([a.elapsed_time(b) for st in up_ev for a, b in st]))
+        g1 = np.array([a.elapsed_time(b) for st in up_ev for a, b in st])
     else:
-        gemm1_ms = float(np.mean([a.elapsed_time(b) for a, b in kev]))
-    print(f"[bench] {K} steps: {ms_per_step:.4f} ms/step (wall {wall:.3f} s)",
-          file=sys.stderr, flush=True)
+        g1 = np.array([a.elapsed_time(b) for a, b in kev])
+    gemm1_ms = float(np.mean(g1))
+    print(f"[bench] {K} steps: median {ms_per_step:.4f} ms/step, mean of the bracket "
+          f"{bracket_ms:.4f} ms (wall {wall:.3f} s)", file=sys.stderr, flush=True)
 
     # -- per-stage times (outside the timed region) ------------------------
     names = ["route", "dispatch", "ffn_up", "ffn_down", "combine"]
@@ -378,11 +408,13 @@ def main():
         bytes1 = wb1 + (rows_loc * row_out + rows_loc * I * ab) * wb1_share
         achieved = bytes1 / (gemm1_ms * 1e6)
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4)}
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                "algorithmic_bytes_per_launch": int(bytes1)}
     else:
         achieved = flops1 / (gemm1_ms * 1e9)
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_MFMA_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4)}
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+                "algorithmic_flops_per_launch": int(flops1)}
     n_loc = max(1, e1 - e0)
     if args.fused:
         kname = "fused_layer_kernel (GEMM-1 + SwiGLU + GEMM-2 + combine, moe_layer_fused)"
@@ -399,6 +431,8 @@ def main():
         kname += f", one launch per micro-batch of {T // NB} tokens"
     roof["kernel"] = kname
     roof["avg_launch_ms"] = round(gemm1_ms, 5)
+    roof["median_launch_ms"] = round(float(np.median(g1)), 5)
+    roof["launches_timed"] = int(len(g1))
     # counters were taken on the workload's own gating only
     roof["traffic"] = None if gate_tag else load_traffic("fused" if args.fused else "gemm1",
                                                          cfg.name)
@@ -411,6 +445,12 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "timing": {"per_step": "median of per-step HIP events on the launch stream",
+                   "mean_ms_per_step": round(float(np.mean(step_ms)), 5),
+                   "min_ms_per_step": round(float(np.min(step_ms)), 5),
+                   "bracket_ms_per_step": round(bracket_ms, 5),
+                   "mall_flush_between_steps": bool(flush_buf is not None),
+                   "graph_replay": graph is not None},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -539,7 +579,7 @@ def stats_summary(stats_csv, out_path, workload="c2", extra=""):
     lines = ["# rocprofv3 --kernel-trace --stats: per-kernel totals (ns), workload " + workload,
              "# command (from /tmp, TMPDIR=/tmp, R = repository root):",
              "#   rocprofv3 --kernel-trace --stats -f csv -d <dir> -o st -- python3 $R/bench.py "
-             f"--config {workload} --steps 5 --warmup 2 --no-cpu-baseline {extra}".rstrip(),
+             f"--config {workload} --no-cpu-baseline {extra}".rstrip(),
              f"#   python3 $R/bench.py --config {workload} --stats-summary "
              "<dir>/st_kernel_stats.csv <out>",
              "# input generation kernels (torch elementwise ops) run before the timed steps",
@@ -558,17 +598,30 @@ def stats_summary(stats_csv, out_path, workload="c2", extra=""):
             if r["Kernel_Name"].startswith(("void moe::", "moe::")):
                 per.setdefault(r["Kernel_Name"], []).append(
                     int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-        lines.append("# median ns per dispatch (kernel trace), dispatches, kernel")
+        lines.append("# median ns, mean ns per dispatch (kernel trace), dispatches, kernel")
         for k, v in sorted(per.items(), key=lambda kv: -statistics.median(kv[1])):
-            lines.append(f"# {statistics.median(v):.0f}, {len(v)}, {k[:120]}")
+            lines.append(f"# {statistics.median(v):.0f}, {statistics.fmean(v):.0f}, "
+                         f"{len(v)}, {k[:120]}")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines[:30]))
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(cfg, inp, sample_tokens: int):
-    """The oracle, as it stands, on the first S tokens of the same workload."""
-    import numpy as np
+    """The oracle, as it stands, on the first S tokens of the same workload,
+    timed per stage (route, dispatch, expert FFN, combine)."""
     from oracle import moe_oracle as O
     from oracle.torch_io import stored
     try:
@@ -587,14 +640,17 @@ def cpu_baseline(cfg, inp, sample_tokens: int):
                       inv_temperature=sub.inv_temperature, min_prob=sub.min_prob,
                       fp8_dispatch=sub.fp8_dispatch)
     yr = st["y_remote"][: S * cfg.k] if st["y_remote"] is not None else None
+    stages = {}
     t0 = time.perf_counter()
     O.layer_forward(p, st["x"][:S], st["w_router"], st["bias"], st["w13"], st["w2"],
-                    st["w13_scale"], st["w2_scale"], yr)
+                    st["w13_scale"], st["w2_scale"], yr, timings=stages)
     dt = time.perf_counter() - t0
     return {"value": round(S / dt, 2), "unit": "tokens/s", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": _cpu_model(),
+            "stages_s": {k: round(v, 3) for k, v in stages.items()},
             "sample": f"first {S} of {cfg.T} tokens of the {cfg.name} layer, full "
-                      f"expert weights, float64 numpy oracle; {dt:.1f} s"}
+                      f"expert weights, float64 numpy oracle on {cores} BLAS threads; "
+                      f"{dt:.1f} s"}
 
 
 if __name__ == "__main__":

@@ -20,6 +20,8 @@ DTYPE_F32, DTYPE_F16, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2, 3
 GATE_SOFTMAX, GATE_SIGMOID = 0, 1
 ACT_SWIGLU, ACT_GELU = 0, 1
 WS_DISPATCH, WS_FFN, WS_FUSED = 0, 1, 2
+# byte offset of moe_layer_fused's status word in its workspace (include/moe.h)
+FUSED_STATUS_BYTE = 32
 
 EXPORTS = ["moe_route", "moe_dispatch", "moe_dispatch_fp8", "moe_expert_ffn",
            "moe_expert_ffn_up", "moe_expert_ffn_up_fp8", "moe_expert_ffn_down",

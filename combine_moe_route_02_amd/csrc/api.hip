@@ -126,6 +126,8 @@ int moe_expert_ffn_up(const void* x_perm, const int32_t* offsets, int act_dtype,
   if (w_dtype == MOE_DTYPE_FP8_E4M3 && !w13_scale) return MOE_ERR_ARG;
   if (ws && ws_bytes < ffn_ws_bytes()) return MOE_ERR_WORKSPACE;
   const int Nb = act == MOE_ACT_SWIGLU ? 2 * I : I;
+  // 16-bit tiles cut the weight rows (2I for SwiGLU, I for GELU) into 256s
+  if (act_dtype != MOE_DTYPE_F32 && (H % 256 || Nb % 256)) return MOE_ERR_UNSUPPORTED;
   GemmArgs a{};
   ffn_ws_attach(a, ws, ws_bytes);
   a.A = x_perm;

@@ -14,6 +14,8 @@
 //   layout_one_tile  hist + scan + slots in one block for T <= 256
 //   layout_few_experts  hist + scan + slots in one launch for E <= 32: every
 //           block counts all picks, then ranks its own tile's
+//   layout_count_all  the same in one launch for more experts (LDS
+//           histograms), up to kCountAllMaxPicks picks
 //   hist    per-tile expert histogram (LDS integer atomics: exact counts)
 //   scan    per-expert prefix over tiles -> tile bases, counts, offsets
 //   slots   rank of each pick among earlier picks of the same expert:
@@ -381,6 +383,131 @@ __global__ void __launch_bounds__(TILE)
   }
 }
 
+// Whole layout of a multi-tile batch with many experts (up to 1024) in one
+// launch, one block per 256-token tile, the counterpart of the kernel above
+// for expert counts too large for register counters: every block counts all
+// picks of the batch into two LDS histograms, the picks before its own tile
+// and the rest (one LDS atomic add per pick; exact integer counts, so the
+// order of the atomics does not matter), which gives the totals (counts,
+// offsets) and its tile base; then its tile's slots exactly as in
+// slots_kernel.  The work grows with tiles x picks, so the host uses it up
+// to kCountAllMaxPicks picks and the three-kernel path above that.
+// NT threads share the counting; the first TILE of them own the tile's
+// tokens.
+constexpr long long kCountAllMaxPicks = 262144;
+
+template <int KMAX, int NT>
+__global__ void __launch_bounds__(NT)
+    layout_count_all_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
+                            int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                            int32_t* __restrict__ slot_of, int32_t* __restrict__ row_token) {
+  extern __shared__ uint64_t dyn[];
+  uint64_t* lanes_of = dyn;                  // [4][E] lane masks of this tile
+  int* h_bef = (int*)(lanes_of + 4 * E);     // [E] picks before this tile
+  int* h_rest = h_bef + E;                   // [E] picks from this tile on
+  int* wbase = h_rest + E;                   // [4][E] exclusive prefix over waves
+  int* s_base = wbase + 4 * E;               // [E] offsets[e] + h_bef[e]
+  __shared__ int s_part[NT];
+  const int tile = (int)blockIdx.x;
+  const int tid = (int)threadIdx.x;
+  const int wave = tid >> 6;
+  for (int i = tid; i < 4 * E; i += NT) lanes_of[i] = 0;
+  for (int i = tid; i < 2 * E; i += NT) h_bef[i] = 0;
+  // this tile's picks (owned by the first TILE threads)
+  const int t = tile * TILE + tid;
+  const bool valid = tid < TILE && t < T;
+  int pk[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) pk[j] = (valid && j < k) ? idx[(long long)t * k + j] : -1;
+  __syncthreads();
+  // count every pick: before this tile into h_bef, the rest into h_rest;
+  // 16-byte loads, U of them in flight per thread
+  {
+    const int n_all = T * k, n_bef = tile * TILE * k;  // n_bef is a multiple of 4
+    const int v_end = n_all >> 2;
+    constexpr int U = 8;
+    for (int v0 = tid; v0 < v_end; v0 += U * NT) {
+      int4 q[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (v0 + u * NT < v_end) q[u] = ((const int4*)idx)[v0 + u * NT];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (v0 + u * NT >= v_end) break;
+        int* h = (v0 + u * NT) * 4 < n_bef ? h_bef : h_rest;
+        if (q[u].x >= 0) atomicAdd(&h[q[u].x], 1);  // -1: dropped by the threshold
+        if (q[u].y >= 0) atomicAdd(&h[q[u].y], 1);
+        if (q[u].z >= 0) atomicAdd(&h[q[u].z], 1);
+        if (q[u].w >= 0) atomicAdd(&h[q[u].w], 1);
+      }
+    }
+    for (int n = (v_end << 2) + tid; n < n_all; n += NT) {  // the last n_all % 4
+      const int e = idx[n];
+      if (e >= 0) atomicAdd(&h_rest[e], 1);
+    }
+  }
+  // lane masks of this tile's picks per wave and expert
+  const uint64_t bit = 1ull << lane_id();
+  if (valid)
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (pk[j] >= 0) atomicOr((unsigned long long*)&lanes_of[wave * E + pk[j]], bit);
+  __syncthreads();
+  // offsets: exclusive scan over experts of the totals; thread i owns the
+  // contiguous experts [i * per, (i + 1) * per)
+  const int per = (E + NT - 1) / NT;
+  int run_total = 0;
+  for (int q = 0; q < per; ++q) {
+    const int e = tid * per + q;
+    if (e < E) run_total += h_bef[e] + h_rest[e];
+  }
+  s_part[tid] = run_total;
+  __syncthreads();
+  for (int o = 1; o < NT; o <<= 1) {
+    const int add = tid >= o ? s_part[tid - o] : 0;
+    __syncthreads();
+    s_part[tid] += add;
+    __syncthreads();
+  }
+  int base = s_part[tid] - run_total;
+  for (int q = 0; q < per; ++q) {
+    const int e = tid * per + q;
+    if (e < E) {
+      const int c = h_bef[e] + h_rest[e];
+      s_base[e] = base + h_bef[e];
+      if (tile == 0) {
+        counts[e] = c;
+        offsets[e] = base;
+      }
+      base += c;
+    }
+  }
+  if (tile == 0 && tid == NT - 1) offsets[E] = s_part[NT - 1];
+  for (int e = tid; e < E; e += NT) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      wbase[w * E + e] = run;
+      run += __popcll(lanes_of[w * E + e]);
+    }
+  }
+  __syncthreads();
+  if (!valid) return;
+  const uint64_t lt = bit - 1;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j >= k) break;
+    const int e = pk[j];
+    if (e < 0) {  // dropped pick: no row
+      slot_of[(long long)t * k + j] = -1;
+      continue;
+    }
+    const int r = s_base[e] + wbase[wave * E + e] + __popcll(lanes_of[wave * E + e] & lt);
+    slot_of[(long long)t * k + j] = r;
+    row_token[r] = t;
+  }
+}
+
 // One wave per token; rows of local experts only.  KMAX >= k bounds the
 // unrolled pick loop so the (wave-uniform) row numbers stay in registers.
 template <int KMAX>
@@ -534,6 +661,14 @@ int dispatch_impl(const void* x, int act_dtype, const int32_t* idx, int T, int H
   } while (0)
     MOE_BY_K(MOE_LAYOUTF);
 #undef MOE_LAYOUTF
+  } else if (n_tiles > 1 && (long long)T * k <= kCountAllMaxPicks) {
+    // lane masks, two histograms, wave bases and tile bases (dynamic LDS)
+    const size_t lds = (size_t)E * (4 * sizeof(uint64_t) + 7 * sizeof(int));
+#define MOE_LAYOUTC(KM)                                                                  \
+  hipLaunchKernelGGL((layout_count_all_kernel<KM, 512>), dim3(n_tiles), dim3(512), lds, s, \
+                     idx, T, E, k, counts, offsets, slot_of, row_token)
+    MOE_BY_K(MOE_LAYOUTC);
+#undef MOE_LAYOUTC
   } else {
     if (n_tiles > 0) {
       hipLaunchKernelGGL(hist_kernel, dim3(n_tiles), dim3(TILE), E * sizeof(int), s, idx,

@@ -34,6 +34,10 @@ namespace {
 
 constexpr int kQueues = 8;
 constexpr int kHeaderInts = 16;          // queue counters, error flag, padding
+// The error flag (header int kQueues) is cleared with the header before every
+// launch and raised by a timed-out wait, so after the call it is the call's
+// status word at the byte offset the header documents.
+static_assert(kQueues * 4 == MOE_FUSED_STATUS_BYTE, "status word offset");
 constexpr int kTokensPerItem = 64;       // combine block (16 tokens per wave)
 constexpr int kSpinLimit = 1 << 20;      // ~seconds of sleeping spins
 

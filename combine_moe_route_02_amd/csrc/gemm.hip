@@ -569,11 +569,6 @@ __global__ void __launch_bounds__(WM * WN * 64)
   Tile::run(p, ti, nt, smem, nullptr, &ks);
 }
 
-__global__ void __launch_bounds__(256) zero_split_counters(int* c, int n) {
-  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
-  if (i < n) c[i] = 0;
-}
-
 // Plain fp32 grouped GEMM (64x64 tiles, 4x4 outputs per thread).
 template <int EPI>
 __global__ void __launch_bounds__(256) grouped_gemm_f32(GemmArgs p) {
@@ -738,10 +733,6 @@ int run_dma(GemmArgs a, int max_rows, int gm, hipStream_t s) {
   if (a.split_ws && ((long long)grid.x * Tile::SLOT > a.split_slots * 65536ll ||
                      (long long)grid.x * 4 > kSplitCounterBytes))
     a.split_ws = nullptr;
-  if (a.split_ws) {
-    hipLaunchKernelGGL(zero_split_counters, dim3((grid.x + 255) / 256), dim3(256), 0, s,
-                       a.split_cnt, (int)grid.x);
-  }
   hipLaunchKernelGGL(kern, grid, dim3(WM * WN * 64), 0, s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

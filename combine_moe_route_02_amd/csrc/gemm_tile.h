@@ -306,7 +306,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // [k0, k0 + nk) (of BK each); with parts > 1 it stores its fp32 partial sums
 // in its own slot, and the last of the `parts` workgroups to arrive adds all
 // slots in part order (so the result does not depend on arrival order) and
-// runs the epilogue.  Part s's slot is slot0 + s * slot_step floats; each
+// runs the epilogue.  The arrival counter starts at zero and the last
+// arriver puts it back to zero, so a workspace zeroed once stays usable
+// without a clearing launch before every GEMM.  Part s's slot is slot0 + s * slot_step floats; each
 // thread owns a contiguous run of NACC floats in it (the tile's accumulators
 // per thread: 256 for a 256x256 tile).
 struct KSplit {
@@ -718,7 +720,12 @@ do {                                                                            
         const int old = __hip_atomic_fetch_add(ks->counter, 1, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT);
         *ks->s_flag = old == ks->parts - 1;
-        if (old == ks->parts - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if (old == ks->parts - 1) {
+          // every part has arrived: the counter goes back to zero for the
+          // next launch (the kernel boundary orders it before that launch)
+          __hip_atomic_store(ks->counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
       }
       __syncthreads();
       if (!*ks->s_flag) return;

@@ -85,11 +85,12 @@ class MoELayer:
         nb = L.moe_workspace_bytes(L.WS_DISPATCH, s.T, s.H, s.E_disp, s.k, s.I)
         self.ws = torch.empty((max(nb, 16),), dtype=torch.uint8, device=dev)
         self.ws_fused = None
-        # FFN workspace: lets the GEMMs split a sparse last round of tiles over K
+        # FFN workspace: lets the GEMMs split a sparse last round of tiles over
+        # K; its arrival counters must start at zero (the calls keep them so)
         self.ws_ffn = None
         if ffn_split:
             nf = L.moe_workspace_bytes(L.WS_FFN, s.T, s.H, s.E_disp, s.k, s.I)
-            self.ws_ffn = torch.empty((nf,), dtype=torch.uint8, device=dev)
+            self.ws_ffn = torch.zeros((nf,), dtype=torch.uint8, device=dev)
 
     # -- the four calls -----------------------------------------------------
     # -- placement hooks ------------------------------------------------------
@@ -187,7 +188,7 @@ class MoELayer:
         e0, e1 = s.local
         if self.ws_fused is None:
             nb = L.moe_workspace_bytes(L.WS_FUSED, s.T, s.H, s.E_disp, s.k, s.I)
-            self.ws_fused = torch.empty((max(nb, 16),), dtype=torch.uint8,
+            self.ws_fused = torch.zeros((max(nb, 64),), dtype=torch.uint8,
                                         device=self.out.device)
         L.moe_layer_fused(x, self.offsets, self.slot_of, self.row_token, self.topk_w,
                           s.E_disp, s.I, e0, e1, ACTS[s.act], w13, w2, self.h, self.y_perm,
@@ -200,10 +201,25 @@ class MoELayer:
         L.moe_dispatch(x, self.topk_disp, s.E_disp, 0, 0, self.counts, self.offsets,
                        self.slot_of, self.row_token, self.x_perm, self.ws, stream=stream)
 
+    def fused_status(self) -> int:
+        """Status word of the last completed moe_layer_fused call: 0, or 1 if a
+        readiness wait timed out (out, y_perm and h may then be partly written).
+        Reading it waits for the device."""
+        if self.ws_fused is None:
+            return 0
+        return int(self.ws_fused[L.FUSED_STATUS_BYTE:L.FUSED_STATUS_BYTE + 4]
+                   .view(torch.int32).item())
+
     def forward_fused(self, x, w_router, bias, w13, w2, stream=None) -> torch.Tensor:
+        """The whole layer with the fused kernel; raises if its status word
+        reports a timed-out wait."""
         self.route(x, w_router, bias, stream)
         self.dispatch_layout(x, stream)
         self.fused(x, w13, w2, stream)
+        st = self.fused_status()
+        if st != 0:
+            raise L.MoeError("moe_layer_fused", st, "a readiness wait timed out; the "
+                             "outputs are incomplete")
         return self.out
 
 
@@ -237,7 +253,7 @@ class MicrobatchedLayer:
             self.layers.append(lay)
         if ffn_split:
             nf = L.moe_workspace_bytes(L.WS_FFN, spec.T, spec.H, spec.E_disp, spec.k, spec.I)
-            ws = torch.empty((nf,), dtype=torch.uint8, device=dev)
+            ws = torch.zeros((nf,), dtype=torch.uint8, device=dev)
             for lay in self.layers:
                 lay.ws_ffn = ws
         self.s_mem = torch.cuda.Stream(dev)

@@ -207,13 +207,19 @@ int moe_expert_ffn_up_fp8(const void* x_perm_q, const float* x_scale,
  *             most half busy, those tiles are split over K: each part stores
  *             fp32 partial sums in the workspace and the last part to finish
  *             adds them in part order (deterministic for a given GPU) before
- *             the epilogue.  Contents need not be initialised; calls that
- *             share a workspace must be ordered (same stream).  A non-NULL
- *             workspace that is too small returns MOE_ERR_WORKSPACE.
+ *             the epilogue.  Its first 16 KB are arrival counters: they must
+ *             be zero before the workspace is first used (zero-fill it once
+ *             when it is allocated); every call leaves them zero again, so
+ *             no clearing is needed between calls.  The rest need not be
+ *             initialised.  Calls that share a workspace must be ordered
+ *             (same stream).  A non-NULL workspace that is too small
+ *             returns MOE_ERR_WORKSPACE.
  * Computation: fp32 accumulation; SwiGLU h = silu(x Wg^T) * (x Wu^T), GELU
  * h = gelu_erf(x W1^T), h rounded once to act_dtype; y = h W2^T rounded once.
- * Limits: H % 256 == 0 and I % 128 == 0 for 16-bit types; fp32 needs
- * H % 64 == 0 and I % 64 == 0.
+ * Limits: 16-bit types need H % 256 == 0, and I % 128 == 0 with SwiGLU or
+ * I % 256 == 0 with GELU (the first GEMM's weight rows, 2I or I, are cut
+ * into 256-row tiles); fp32 needs H % 64 == 0 and I % 64 == 0.  Other sizes
+ * return MOE_ERR_UNSUPPORTED before anything is launched.
  */
 int moe_expert_ffn(const void* x_perm, const int32_t* offsets, int act_dtype,
                    int H, int I, int e_begin, int e_end, int max_rows, int act,
@@ -268,9 +274,21 @@ int moe_combine(const void* y_perm, const int32_t* slot_of,
  * Results equal moe_expert_ffn (without workspace) followed by
  * moe_combine, bit for bit: h_ws, y_perm (local rows) and out are written
  * (dropped picks, slot_of -1, as in moe_combine).  ws must hold
- * moe_workspace_bytes(MOE_WS_FUSED, ...) bytes; it is initialised by the
- * call.  Supported for 16-bit activations with 16-bit weights.
+ * moe_workspace_bytes(MOE_WS_FUSED, ...) bytes of queue and readiness
+ * counters; the call clears them itself (a small kernel before the fused
+ * one), so their contents need not be initialised.  Calls sharing a
+ * workspace must be ordered (same stream).
+ * Status: the int32 at byte offset 32 of ws (MOE_FUSED_STATUS_BYTE) holds
+ * the call's status once the call has completed: 0, or 1 when a readiness
+ * wait exceeded its bounded spin (about a second; only possible if the
+ * device cannot run the kernel's workgroups to completion, for instance
+ * when other work keeps one XCD's compute units busy), in which case h_ws,
+ * y_perm and out may be incomplete.  The caller reads it after the call has
+ * completed (after a stream synchronisation or an event), without any
+ * library call.
+ * Supported for 16-bit activations with 16-bit weights and SwiGLU.
  */
+#define MOE_FUSED_STATUS_BYTE 32
 int moe_layer_fused(const void* x, const int32_t* offsets,
                     const int32_t* slot_of, const int32_t* row_token,
                     const float* topk_w, int act_dtype, int T, int H, int E,
@@ -321,9 +339,9 @@ int moe_expert_load_stats(const int32_t* topk_idx, int T, int k, int E,
                           uint64_t* stats, hipStream_t stream);
 
 /* Workspace bytes needed by moe_dispatch (MOE_WS_DISPATCH), moe_expert_ffn
- * and its halves (MOE_WS_FFN: one 256 KB partial-sum slot per compute unit
- * of the current device, plus counters) or moe_layer_fused (MOE_WS_FUSED)
- * for these sizes. */
+ * and its halves (MOE_WS_FFN: 16 KB of counters, zero-filled once by the
+ * caller, then one 256 KB partial-sum slot per compute unit of the current
+ * device) or moe_layer_fused (MOE_WS_FUSED) for these sizes. */
 size_t moe_workspace_bytes(int which, int T, int H, int E, int k, int I);
 
 /* Static, human-readable text for a status code. */

@@ -52,6 +52,7 @@ them, and the byte arithmetic printed on the pages.
 from __future__ import annotations
 
 import math
+import time
 from dataclasses import dataclass
 from typing import Dict, Optional, Sequence
 
@@ -507,7 +508,8 @@ def layer_forward(p: LayerParams, x_stored: np.ndarray,
                   w2_scale: Optional[np.ndarray] = None,
                   y_remote_stored: Optional[np.ndarray] = None,
                   logits: Optional[np.ndarray] = None,
-                  placement=None) -> Dict[str, np.ndarray]:
+                  placement=None,
+                  timings: Optional[Dict[str, float]] = None) -> Dict[str, np.ndarray]:
     """The full layer on stored inputs (bit patterns / float32 values).
 
     ``logits`` may be given (float32) instead of being computed from the
@@ -519,11 +521,23 @@ def layer_forward(p: LayerParams, x_stored: np.ndarray,
     ``placement`` = (rep_offsets, rep_phys, E_phys) replaces every logical
     pick by its physical copy (place_experts) before dispatch; the expert
     range and the weights are then those of the physical slots.
+
+    ``timings``, when given, receives the wall-clock seconds of the four
+    stages (route, dispatch, ffn, combine); it changes nothing computed.
     """
+    clock = [time.perf_counter()]
+
+    def lap(stage):
+        if timings is not None:
+            now = time.perf_counter()
+            timings[stage] = timings.get(stage, 0.0) + now - clock[0]
+            clock[0] = now
+
     x64 = decode(x_stored, p.act_dtype)
     if logits is None:
         logits = router_logits(x64, decode(w_router_stored, p.act_dtype))
     idx, w = route(logits, bias, p.k, p.gate, p.renorm, p.inv_temperature, p.min_prob)
+    lap("route")
     E = p.E
     idx_log = idx
     if placement is not None:
@@ -541,6 +555,7 @@ def layer_forward(p: LayerParams, x_stored: np.ndarray,
         xp64 = e4m3_decode(x_perm) * x_scale.astype(np.float64)[:, None]
     else:
         xp64 = decode(x_perm, p.act_dtype)
+    lap("dispatch")
 
     N = p.T * p.k
     if y_remote_stored is not None:
@@ -554,7 +569,9 @@ def layer_forward(p: LayerParams, x_stored: np.ndarray,
             continue
         w13, w2 = expert_weights(p, w13_stored, w2_stored, w13_scale, w2_scale, el)
         y_perm[r0 + a:r0 + b] = expert_ffn(xp64[a:b], w13, w2, p.act, p.act_dtype)
+    lap("ffn")
     out = combine(y_perm, slot_of, w, p.act_dtype)
+    lap("combine")
     return dict(logits=logits, topk_idx=idx_log, topk_phys=idx, topk_w=w, counts=counts,
                 offsets=offsets, slot_of=slot_of, row_token=row_token,
                 x_perm=x_perm, x_scale=x_scale, y_perm=y_perm, out=out)

@@ -112,6 +112,13 @@ def test_ffn_validation():
              L.DTYPE_BF16, FAKE, FAKE, None, 0, None) == L.MOE_ERR_UNSUPPORTED
     assert f(FAKE, FAKE, L.DTYPE_BF16, 256, 96, 0, 8, 64, 0, FAKE, None, FAKE, None,
              L.DTYPE_BF16, FAKE, FAKE, None, 0, None) == L.MOE_ERR_UNSUPPORTED
+    # 16-bit GELU cuts its I weight rows into 256-row tiles: I % 256 == 0
+    for I in (128, 384):
+        assert f(FAKE, FAKE, L.DTYPE_BF16, 256, I, 0, 8, 64, L.ACT_GELU, FAKE, None, FAKE,
+                 None, L.DTYPE_BF16, FAKE, FAKE, None, 0, None) == L.MOE_ERR_UNSUPPORTED
+        assert lib.moe_expert_ffn_up(FAKE, FAKE, L.DTYPE_F16, 256, I, 0, 8, 64, L.ACT_GELU,
+                                     FAKE, None, L.DTYPE_F16, FAKE, None, 0,
+                                     None) == L.MOE_ERR_UNSUPPORTED
     # bad activation and range
     assert f(FAKE, FAKE, L.DTYPE_BF16, 256, 128, 0, 8, 64, 5, FAKE, None, FAKE, None,
              L.DTYPE_BF16, FAKE, FAKE, None, 0, None) == L.MOE_ERR_ARG

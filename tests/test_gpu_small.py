@@ -276,3 +276,35 @@ def test_fp8_dispatch_accuracy_against_the_16bit_transport():
     say(f"  fp8 vs bf16 transport: out rel-L2 GPU {gpu_delta:.4f}, oracle {ora_delta:.4f}")
     assert 0.005 < ora_delta < 0.08
     assert abs(gpu_delta - ora_delta) <= 0.2 * ora_delta
+
+
+# (T, E, k): one tile; few experts; many experts counted by every block (up to
+# 262144 picks, including 1024 experts at k = 32 and few experts past the
+# few-experts limit); the three-kernel path above 262144 picks
+LAYOUT_CASES = [(200, 256, 8), (3000, 16, 4), (5000, 64, 8), (1100, 1024, 32),
+                (20000, 8, 2), (33000, 256, 8), (40000, 64, 8)]
+
+
+@pytest.mark.parametrize("T,E,k", LAYOUT_CASES, ids=[f"T{t}_E{e}_k{k}" for t, e, k in LAYOUT_CASES])
+def test_dispatch_layout_paths(T, E, k):
+    """Counts, offsets, the layout map and x_perm, bit for bit against the
+    oracle, on every layout kernel, with a skewed expert load (a few hot
+    experts) and a local range in the middle of the experts."""
+    from combine_moe_route_02_amd import MoELayer
+    e0, e1 = E // 4, E // 4 + max(1, E // 2)
+    cfg = small(f"layout_{T}_{E}_{k}", T, 64, E, k, 128, e_begin=e0, e_end=e1,
+                seed_off=70 + E % 97)
+    g = torch.Generator().manual_seed(T + E + k)
+    s = torch.randn((T, E), generator=g)
+    bias = torch.zeros(E)
+    bias[torch.randperm(E, generator=g)[:3]] = 2.0     # three hot experts
+    x = torch.randn((T, 64), generator=g).to(torch.bfloat16)
+    say(f"[gpu] dispatch layout T={T} E={E} k={k} local=[{e0},{e1})")
+    lay = MoELayer(spec(cfg), "cuda")
+    lay.logits.copy_(s.cuda())
+    lay.route_from_logits(bias.cuda())
+    lay.dispatch(x.cuda())
+    torch.cuda.synchronize()
+    st = {"x": stored(x), "bias": bias.numpy()}
+    r = check_routing(cfg, lay, st)
+    assert int(r["offsets"][-1]) == T * k
