@@ -14,8 +14,9 @@
 //   layout_one_tile  hist + scan + slots in one block for T <= 256
 //   layout_few_experts  hist + scan + slots in one launch for E <= 32: every
 //           block counts all picks, then ranks its own tile's
-//   layout_count_all  the same in one launch for more experts (LDS
-//           histograms), up to kCountAllMaxPicks picks
+//   slots_from_table  after hist: totals, offsets, tile bases and slots in
+//           one kernel for up to kTableMaxTiles tiles (every block reads
+//           the whole tile-count table)
 //   hist    per-tile expert histogram (LDS integer atomics: exact counts)
 //   scan    per-expert prefix over tiles -> tile bases, counts, offsets
 //   slots   rank of each pick among earlier picks of the same expert:
@@ -383,87 +384,65 @@ __global__ void __launch_bounds__(TILE)
   }
 }
 
-// Whole layout of a multi-tile batch with many experts (up to 1024) in one
-// launch, one block per 256-token tile, the counterpart of the kernel above
-// for expert counts too large for register counters: every block counts all
-// picks of the batch into two LDS histograms, the picks before its own tile
-// and the rest (one LDS atomic add per pick; exact integer counts, so the
-// order of the atomics does not matter), which gives the totals (counts,
-// offsets) and its tile base; then its tile's slots exactly as in
-// slots_kernel.  The work grows with tiles x picks, so the host uses it up
-// to kCountAllMaxPicks picks and the three-kernel path above that.
-// NT threads share the counting; the first TILE of them own the tile's
-// tokens.
-constexpr long long kCountAllMaxPicks = 262144;
+// Layout of a multi-tile batch with many experts after hist_kernel: one
+// block per 256-token tile reads the whole tile-count table (each thread the
+// row of its experts, 16 bytes at a time), which gives every expert's total
+// (counts, offsets by a block scan over experts) and its picks before this
+// tile (the tile base); then its tile's slots exactly as in slots_kernel.
+// Two launches instead of histogram, scan and slots.  Every block reads the
+// whole table, so the host uses it up to kTableMaxTiles tiles.
+constexpr int kTableMaxTiles = 256;
 
-template <int KMAX, int NT>
-__global__ void __launch_bounds__(NT)
-    layout_count_all_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
+template <int KMAX>
+__global__ void __launch_bounds__(TILE)
+    slots_from_table_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
+                            int n_tiles, const int32_t* __restrict__ tile_counts,
                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                             int32_t* __restrict__ slot_of, int32_t* __restrict__ row_token) {
   extern __shared__ uint64_t dyn[];
   uint64_t* lanes_of = dyn;                  // [4][E] lane masks of this tile
-  int* h_bef = (int*)(lanes_of + 4 * E);     // [E] picks before this tile
-  int* h_rest = h_bef + E;                   // [E] picks from this tile on
-  int* wbase = h_rest + E;                   // [4][E] exclusive prefix over waves
-  int* s_base = wbase + 4 * E;               // [E] offsets[e] + h_bef[e]
-  __shared__ int s_part[NT];
+  int* wbase = (int*)(lanes_of + 4 * E);     // [4][E] exclusive prefix over waves
+  int* s_base = wbase + 4 * E;               // [E] offsets[e] + picks before the tile
+  __shared__ int s_part[TILE];
   const int tile = (int)blockIdx.x;
   const int tid = (int)threadIdx.x;
   const int wave = tid >> 6;
-  for (int i = tid; i < 4 * E; i += NT) lanes_of[i] = 0;
-  for (int i = tid; i < 2 * E; i += NT) h_bef[i] = 0;
-  // this tile's picks (owned by the first TILE threads)
+  for (int i = tid; i < 4 * E; i += TILE) lanes_of[i] = 0;
   const int t = tile * TILE + tid;
-  const bool valid = tid < TILE && t < T;
+  const bool valid = t < T;
   int pk[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) pk[j] = (valid && j < k) ? idx[(long long)t * k + j] : -1;
-  __syncthreads();
-  // count every pick: before this tile into h_bef, the rest into h_rest;
-  // 16-byte loads, U of them in flight per thread
-  {
-    const int n_all = T * k, n_bef = tile * TILE * k;  // n_bef is a multiple of 4
-    const int v_end = n_all >> 2;
-    constexpr int U = 8;
-    for (int v0 = tid; v0 < v_end; v0 += U * NT) {
-      int4 q[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (v0 + u * NT < v_end) q[u] = ((const int4*)idx)[v0 + u * NT];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (v0 + u * NT >= v_end) break;
-        int* h = (v0 + u * NT) * 4 < n_bef ? h_bef : h_rest;
-        if (q[u].x >= 0) atomicAdd(&h[q[u].x], 1);  // -1: dropped by the threshold
-        if (q[u].y >= 0) atomicAdd(&h[q[u].y], 1);
-        if (q[u].z >= 0) atomicAdd(&h[q[u].z], 1);
-        if (q[u].w >= 0) atomicAdd(&h[q[u].w], 1);
-      }
-    }
-    for (int n = (v_end << 2) + tid; n < n_all; n += NT) {  // the last n_all % 4
-      const int e = idx[n];
-      if (e >= 0) atomicAdd(&h_rest[e], 1);
-    }
-  }
-  // lane masks of this tile's picks per wave and expert
-  const uint64_t bit = 1ull << lane_id();
-  if (valid)
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if (pk[j] >= 0) atomicOr((unsigned long long*)&lanes_of[wave * E + pk[j]], bit);
-  __syncthreads();
-  // offsets: exclusive scan over experts of the totals; thread i owns the
-  // contiguous experts [i * per, (i + 1) * per)
-  const int per = (E + NT - 1) / NT;
+  // thread i owns the contiguous experts [i * per, (i + 1) * per): their
+  // totals and their picks before this tile, from the table rows
+  const int per = (E + TILE - 1) / TILE;
   int run_total = 0;
   for (int q = 0; q < per; ++q) {
     const int e = tid * per + q;
-    if (e < E) run_total += h_bef[e] + h_rest[e];
+    if (e >= E) break;
+    const int32_t* row = tile_counts + (long long)e * n_tiles;
+    int bef = 0, tot = 0;
+    int b = 0;
+    if ((n_tiles & 3) == 0) {  // rows start 16-byte aligned: 4 tiles per load
+      for (; b < n_tiles; b += 4) {
+        const int4 v = *(const int4*)(row + b);
+        tot += v.x + v.y + v.z + v.w;
+        bef += (b < tile ? v.x : 0) + (b + 1 < tile ? v.y : 0) + (b + 2 < tile ? v.z : 0) +
+               (b + 3 < tile ? v.w : 0);
+      }
+    }
+    for (; b < n_tiles; ++b) {
+      const int v = row[b];
+      tot += v;
+      bef += b < tile ? v : 0;
+    }
+    s_base[e] = bef;   // picks before the tile for now
+    wbase[e] = tot;    // total for now (wbase is rebuilt below)
+    run_total += tot;
   }
   s_part[tid] = run_total;
   __syncthreads();
-  for (int o = 1; o < NT; o <<= 1) {
+  for (int o = 1; o < TILE; o <<= 1) {
     const int add = tid >= o ? s_part[tid - o] : 0;
     __syncthreads();
     s_part[tid] += add;
@@ -472,18 +451,24 @@ __global__ void __launch_bounds__(NT)
   int base = s_part[tid] - run_total;
   for (int q = 0; q < per; ++q) {
     const int e = tid * per + q;
-    if (e < E) {
-      const int c = h_bef[e] + h_rest[e];
-      s_base[e] = base + h_bef[e];
-      if (tile == 0) {
-        counts[e] = c;
-        offsets[e] = base;
-      }
-      base += c;
+    if (e >= E) break;
+    const int c = wbase[e];
+    s_base[e] += base;
+    if (tile == 0) {
+      counts[e] = c;
+      offsets[e] = base;
     }
+    base += c;
   }
-  if (tile == 0 && tid == NT - 1) offsets[E] = s_part[NT - 1];
-  for (int e = tid; e < E; e += NT) {
+  if (tile == 0 && tid == TILE - 1) offsets[E] = s_part[TILE - 1];
+  __syncthreads();  // the totals in wbase are read; lane masks cleared
+  const uint64_t bit = 1ull << lane_id();
+  if (valid)
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (pk[j] >= 0) atomicOr((unsigned long long*)&lanes_of[wave * E + pk[j]], bit);
+  __syncthreads();
+  for (int e = tid; e < E; e += TILE) {
     int run = 0;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -661,14 +646,16 @@ int dispatch_impl(const void* x, int act_dtype, const int32_t* idx, int T, int H
   } while (0)
     MOE_BY_K(MOE_LAYOUTF);
 #undef MOE_LAYOUTF
-  } else if (n_tiles > 1 && (long long)T * k <= kCountAllMaxPicks) {
-    // lane masks, two histograms, wave bases and tile bases (dynamic LDS)
-    const size_t lds = (size_t)E * (4 * sizeof(uint64_t) + 7 * sizeof(int));
-#define MOE_LAYOUTC(KM)                                                                  \
-  hipLaunchKernelGGL((layout_count_all_kernel<KM, 512>), dim3(n_tiles), dim3(512), lds, s, \
-                     idx, T, E, k, counts, offsets, slot_of, row_token)
-    MOE_BY_K(MOE_LAYOUTC);
-#undef MOE_LAYOUTC
+  } else if (n_tiles > 1 && n_tiles <= kTableMaxTiles) {
+    hipLaunchKernelGGL(hist_kernel, dim3(n_tiles), dim3(TILE), E * sizeof(int), s, idx, T, E,
+                       k, n_tiles, tile_counts);
+    // lane masks, wave bases and tile bases (dynamic LDS)
+    const size_t lds = (size_t)E * (4 * sizeof(uint64_t) + 5 * sizeof(int));
+#define MOE_SLOTST(KM)                                                                  \
+  hipLaunchKernelGGL((slots_from_table_kernel<KM>), dim3(n_tiles), dim3(TILE), lds, s, idx, \
+                     T, E, k, n_tiles, tile_counts, counts, offsets, slot_of, row_token)
+    MOE_BY_K(MOE_SLOTST);
+#undef MOE_SLOTST
   } else {
     if (n_tiles > 0) {
       hipLaunchKernelGGL(hist_kernel, dim3(n_tiles), dim3(TILE), E * sizeof(int), s, idx,

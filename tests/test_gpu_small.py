@@ -278,11 +278,11 @@ def test_fp8_dispatch_accuracy_against_the_16bit_transport():
     assert abs(gpu_delta - ora_delta) <= 0.2 * ora_delta
 
 
-# (T, E, k): one tile; few experts; many experts counted by every block (up to
-# 262144 picks, including 1024 experts at k = 32 and few experts past the
-# few-experts limit); the three-kernel path above 262144 picks
+# (T, E, k): one tile; few experts in one launch; histogram + slots from the
+# tile-count table (up to 256 tiles, including 1024 experts at k = 32 and few
+# experts past the one-launch limit); histogram, scan and slots past 256 tiles
 LAYOUT_CASES = [(200, 256, 8), (3000, 16, 4), (5000, 64, 8), (1100, 1024, 32),
-                (20000, 8, 2), (33000, 256, 8), (40000, 64, 8)]
+                (20000, 8, 2), (33000, 256, 8), (65536, 64, 2), (70000, 64, 2)]
 
 
 @pytest.mark.parametrize("T,E,k", LAYOUT_CASES, ids=[f"T{t}_E{e}_k{k}" for t, e, k in LAYOUT_CASES])
