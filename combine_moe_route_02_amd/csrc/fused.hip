@@ -55,10 +55,16 @@ struct FusedArgs {
 };
 
 // Polls use relaxed agent-scope loads (coherent across XCDs, no cache
-// maintenance); the acquire that invalidates the XCD's L2 runs once, after
-// the condition holds.  Acquire/release at agent scope are whole-L2
-// invalidate/writeback operations on this GPU, so they are kept off the spin
-// path and issued by one thread per workgroup.
+// maintenance).  A producer makes its rows visible with an agent-scope
+// release (a writeback of its XCD's L2) before counting its tile as done.
+// The waiting side needs no agent-scope acquire, which on this GPU
+// invalidates the whole L2 of the XCD (and with it the weight lines the
+// XCD's other workgroups are streaming): the rows a wait guards (h of an
+// m-tile, y_perm rows of local experts) are written once per launch, every
+// cache starts the launch without them, and no workgroup reads them before
+// their producer has written them back and signalled, so no cache can hold
+// a stale copy.  A workgroup-scope acquire orders the later loads after the
+// poll that saw the count.
 __device__ __forceinline__ int load_relaxed(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -76,7 +82,7 @@ __device__ bool block_wait(const int* p, int target, int* err, int* s_flag) {
         break;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     *s_flag = ok;
   }
   __syncthreads();
@@ -188,7 +194,7 @@ __global__ void __launch_bounds__(WM * WN * 64) fused_layer_kernel(FusedArgs f) 
         }
       }
       if (timed_out) break;
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       const float w = lane < f.k ? f.topk_w[(long long)t * f.k + lane] : 0.0f;
       uint4* dst = f.out + (long long)t * f.nch;
       if (f.k <= 8) {

@@ -499,6 +499,20 @@ __global__ void __launch_bounds__(256) grouped_gemm_fp8s(GemmArgs p) {
   }
 }
 
+// Parts per tile of a last round of rem tiles on per workgroups (one XCD's
+// share): when the round leaves at least half the workgroups idle, each tile
+// is split into per / rem parts (at most 8, each of at least 4 k-steps), one
+// per workgroup.  Splitting a fuller round does not pay: measured at the
+// DeepSeek-V3-like share (a 62%-full round split in 3, two parts per
+// workgroup), the partial sums' traffic made GEMM-1 8% slower.
+__device__ __forceinline__ int split_parts(int rem, int per, int nk) {
+  if (2 * rem > per) return 1;
+  int S = per / rem;
+  if (S > 8) S = 8;
+  if (S > nk / 4) S = nk / 4;
+  return S < 1 ? 1 : S;
+}
+
 template <int DT, int EPI, int BM, int BN, int WM, int WN>
 __global__ void __launch_bounds__(WM * WN * 64)
     grouped_gemm_dma(GemmArgs p) {
@@ -510,9 +524,9 @@ __global__ void __launch_bounds__(WM * WN * 64)
   const int total_m = build_mtile_table<Tile::NT, BM>(p, s_pre, s_scan);
   // Each XCD takes a contiguous slice of the tile order; its workgroups take
   // whole rounds of tiles.  The last, partial round (rem tiles for per
-  // workgroups) is split over k when a workspace is given and at most half
-  // the workgroups would otherwise have a tile: S parts per tile, part s of
-  // local tile u on workgroup u * S + s of the XCD.
+  // workgroups) is split over k when a workspace is given and split_parts
+  // says so: S parts per tile, part s of local tile u on workgroup u * S + s
+  // of the XCD.
   const int total = total_m * p.n_tiles;
   const int xcd = (int)blockIdx.x & 7;
   const int per = (int)gridDim.x >> 3;
@@ -522,13 +536,7 @@ __global__ void __launch_bounds__(WM * WN * 64)
   const int full = len / per;
   const int rem = len - full * per;
   const int nk_all = p.K / Tile::BK;
-  int S = 1;
-  if (rem > 0 && p.split_ws != nullptr && 2 * rem <= per) {
-    S = per / rem;
-    if (S > 8) S = 8;
-    if (S > nk_all / 4) S = nk_all / 4;  // at least 4 k-steps per part
-    if (S < 1) S = 1;
-  }
+  const int S = rem > 0 && p.split_ws != nullptr ? split_parts(rem, per, nk_all) : 1;
   for (int r = 0; r < full; ++r) {
     int mt, nt;
     const TileInfo ti = band_tile<BM>(p, s_pre, lo + r * per + idx, p.n_tiles, p.gm, mt, nt);
@@ -553,20 +561,21 @@ __global__ void __launch_bounds__(WM * WN * 64)
     }
     return;
   }
-  if (idx >= rem * S) return;
-  const int u = idx / S, part = idx % S;
-  int mt, nt;
-  const TileInfo ti = band_tile<BM>(p, s_pre, lo + full * per + u, p.n_tiles, p.gm, mt, nt);
-  KSplit ks;
-  ks.k0 = (int)((long long)part * nk_all / S);
-  ks.nk = (int)((long long)(part + 1) * nk_all / S) - ks.k0;
-  ks.parts = S;
-  ks.part = part;
-  ks.slot0 = p.split_ws + (long long)(((u * S) << 3) | xcd) * Tile::SLOT;
-  ks.slot_step = 8 * Tile::SLOT;
-  ks.counter = p.split_cnt + ((u << 3) | xcd);
-  ks.s_flag = &s_flag;
-  Tile::run(p, ti, nt, smem, nullptr, &ks);
+  if (idx < rem * S) {
+    const int u = idx / S, part = idx % S;
+    int mt, nt;
+    const TileInfo ti = band_tile<BM>(p, s_pre, lo + full * per + u, p.n_tiles, p.gm, mt, nt);
+    KSplit ks;
+    ks.k0 = (int)((long long)part * nk_all / S);
+    ks.nk = (int)((long long)(part + 1) * nk_all / S) - ks.k0;
+    ks.parts = S;
+    ks.part = part;
+    ks.slot0 = p.split_ws + (long long)(((u * S) << 3) | xcd) * Tile::SLOT;
+    ks.slot_step = 8 * Tile::SLOT;
+    ks.counter = p.split_cnt + ((u << 3) | xcd);
+    ks.s_flag = &s_flag;
+    Tile::run(p, ti, nt, smem, nullptr, &ks);
+  }
 }
 
 // Plain fp32 grouped GEMM (64x64 tiles, 4x4 outputs per thread).
@@ -814,22 +823,23 @@ inline bool few_rows(const GemmArgs& a, int max_rows) {
 
 template <int DT, int WK, int EPI>
 int pick_tile(GemmArgs a, int max_rows, hipStream_t s) {
-  if (EPI == EPI_F32) {
+  if constexpr (EPI == EPI_F32) {
     // router logits: one n-tile of 256 experts reads each token row once
     if (WK == W_SAME && a.Nb % 256 == 0) return run_dma<DT, EPI, 64, 256, 1, 4>(a, max_rows, 4, s);
     if (WK == W_SAME) return run_dma<DT, EPI, 64, 128, 2, 2>(a, max_rows, 4, s);
     return run_mfma<DT, WK, EPI, 64, 128, 2, 2>(a, max_rows, 4, s);
-  }
-  if (few_rows(a, max_rows)) {
-    if constexpr (WK == W_FP8 && DT == MOE_DTYPE_BF16 && EPI != EPI_F32)
-      return run_fp8s<DT, EPI>(a, max_rows, s);
-    return run_mfma<DT, WK, EPI, 32, 256, 1, 4>(a, max_rows, 1, s);
-  }
-  if constexpr (WK == W_SAME) {
-    if (choose_bm<WK>(a, max_rows) == 256) return run_dma<DT, EPI, 256, 256, 2, 2>(a, max_rows, 8, s);
-    return run_dma<DT, EPI, 128, 256, 2, 2>(a, max_rows, 8, s);
   } else {
-    return run_mfma<DT, WK, EPI, 128, 256, 2, 2>(a, max_rows, 8, s);
+    if (few_rows(a, max_rows)) {
+      if constexpr (WK == W_FP8 && DT == MOE_DTYPE_BF16) return run_fp8s<DT, EPI>(a, max_rows, s);
+      return run_mfma<DT, WK, EPI, 32, 256, 1, 4>(a, max_rows, 1, s);
+    }
+    if constexpr (WK == W_SAME) {
+      if (choose_bm<WK>(a, max_rows) == 256)
+        return run_dma<DT, EPI, 256, 256, 2, 2>(a, max_rows, 8, s);
+      return run_dma<DT, EPI, 128, 256, 2, 2>(a, max_rows, 8, s);
+    } else {
+      return run_mfma<DT, WK, EPI, 128, 256, 2, 2>(a, max_rows, 8, s);
+    }
   }
 }
 

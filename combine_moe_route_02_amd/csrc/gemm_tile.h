@@ -699,7 +699,12 @@ do {                                                                            
     if (ks && ks->parts > 1) {
       // Split tile: publish this part's sums; only the last part to arrive
       // goes on, with the sum of all parts in part order.
-      float* mine = ks->slot0 + ks->part * ks->slot_step + (long long)tid * NACC;
+      // Slot addresses: a uniform base per part plus this thread's 32-bit
+      // byte offset (tid * NACC floats), so every load and store folds the
+      // accumulator offset into its immediate instead of holding a 64-bit
+      // address per value.
+      const uint32_t mine_ofs = (uint32_t)tid * (uint32_t)(NACC * 4);
+      char* mine = (char*)uniform_ptr((const char*)(ks->slot0 + ks->part * ks->slot_step));
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -711,7 +716,7 @@ do {                                                                            
             q[1] = acc_read(acc[i][j][v + 1]);
             q[2] = acc_read(acc[i][j][v + 2]);
             q[3] = acc_read(acc[i][j][v + 3]);
-            *(f32x4*)(mine + (i * TN + j) * NV + v) = q;
+            *(f32x4*)(mine + mine_ofs + ((i * TN + j) * NV + v) * 4) = q;
           }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -729,17 +734,21 @@ do {                                                                            
       }
       __syncthreads();
       if (!*ks->s_flag) return;
-      const float* base = ks->slot0 + (long long)tid * NACC;
+      // the sum of all parts in part order, one 16-byte piece at a time
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
           for (int v = 0; v < NV; v += 4) {
-            const int off = (i * TN + j) * NV + v;
-            f32x4 tot = *(const f32x4*)(base + off);
-            for (int s2 = 1; s2 < ks->parts; ++s2)
-              tot += *(const f32x4*)(base + s2 * ks->slot_step + off);
+            const uint32_t off = mine_ofs + ((i * TN + j) * NV + v) * 4;
+            const char* b0 = (const char*)uniform_ptr((const char*)ks->slot0);
+            f32x4 tot = *(const f32x4*)(b0 + off);
+            for (int s2 = 1; s2 < ks->parts; ++s2) {
+              const char* bs =
+                  (const char*)uniform_ptr((const char*)(ks->slot0 + s2 * ks->slot_step));
+              tot += *(const f32x4*)(bs + off);
+            }
             acc[i][j][v] = tot[0];
             acc[i][j][v + 1] = tot[1];
             acc[i][j][v + 2] = tot[2];

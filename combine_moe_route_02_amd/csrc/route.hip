@@ -33,31 +33,21 @@ __device__ __forceinline__ float key_score(uint64_t key) {
   return __uint_as_float(b);
 }
 
-// One wave per token; EPL = experts per lane (lane l holds e = l + 64*i).
+// Top-k gating of one token by one wave: lane l holds the scores s[i] (bias
+// added) of experts e = l + 64 i, i < EPL (experts past E must not count).
+// k rounds of a wave-wide uint64 max pick the experts in descending order;
+// lane j < k writes the j-th pick and its gate weight.
 template <int EPL>
-__global__ void __launch_bounds__(256)
-    topk_gate_kernel(const float* __restrict__ logits, const float* __restrict__ bias,
-                     int T, int E, int k, int gate, int renorm, float inv_temp,
-                     float min_prob, int32_t* __restrict__ topk_idx,
-                     float* __restrict__ topk_w) {
+__device__ __forceinline__ void topk_token(const float (&s)[EPL], int E, int k, int gate,
+                                           int renorm, float inv_temp, float min_prob,
+                                           int32_t* __restrict__ idx_row,
+                                           float* __restrict__ w_row) {
   const int lane = lane_id();
-  const int t = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
-  if (t >= T) return;
-  const float* lg = logits + (long long)t * E;
-  float s[EPL];
   uint64_t key[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + 64 * i;
-    if (e < E) {
-      float v = lg[e];
-      if (bias) v = v + bias[e];
-      s[i] = v;
-      key[i] = select_key(v, e);
-    } else {
-      s[i] = 0.0f;
-      key[i] = 0;  // below every real key
-    }
+    key[i] = e < E ? select_key(s[i], e) : 0;  // 0: below every real key
   }
   uint64_t mine = 0;  // lane j keeps the j-th pick
   for (int j = 0; j < k; ++j) {
@@ -92,9 +82,143 @@ __global__ void __launch_bounds__(256)
     w = tot > 0.0f ? w / tot : 0.0f;
   }
   if (lane < k) {
-    topk_idx[(long long)t * k + lane] = keep ? (int32_t)(~(uint32_t)mine) : -1;
-    topk_w[(long long)t * k + lane] = w;
+    idx_row[lane] = keep ? (int32_t)(~(uint32_t)mine) : -1;
+    w_row[lane] = w;
   }
+}
+
+// Max and sum over the 16 lanes of this lane's DPP row (lanes 16 r .. 16 r +
+// 15), every lane receiving the result: four row rotations by 1, 2, 4 and 8
+// lanes (v_mov_b32_dpp row_ror), no LDS permute.  The max is exact; the sum's
+// association depends on the lane, so lanes may differ in the last bit.
+__device__ __forceinline__ uint64_t row16_max_u64(uint64_t v) {
+#define MOE_ROW_MAX(CTRL)                                                                  \
+  do {                                                                                     \
+    const uint32_t lo_ = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xf,  \
+                                                            0xf, false);                  \
+    const uint32_t hi_ = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, \
+                                                            0xf, 0xf, false);             \
+    const uint64_t w_ = ((uint64_t)hi_ << 32) | lo_;                                       \
+    v = w_ > v ? w_ : v;                                                                   \
+  } while (0)
+  MOE_ROW_MAX(0x121);
+  MOE_ROW_MAX(0x122);
+  MOE_ROW_MAX(0x124);
+  MOE_ROW_MAX(0x128);
+#undef MOE_ROW_MAX
+  return v;
+}
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x121, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x122, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
+  return v;
+}
+
+// Top-k gating of four tokens at once, one 16-lane row of the wave each:
+// lane 16 g + r holds the scores s[i] (bias added) of experts e = r + 16 i,
+// i < EPL, of the row's token (experts past E must not count).  The same
+// selection as topk_token, with the k rounds' maxima taken over the row by
+// DPP rotations, so the four tokens' dependency chains interleave and no
+// round waits on an LDS permute.  Lane r < k of a row writes that token's
+// r-th pick when `valid`; k <= 16.
+template <int EPL>
+__device__ __forceinline__ void topk_token16(const float (&s)[EPL], int E, int k, int gate,
+                                             int renorm, float inv_temp, float min_prob,
+                                             bool valid, int32_t* __restrict__ idx_row,
+                                             float* __restrict__ w_row) {
+  const int r = lane_id() & 15;
+  uint64_t key[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = r + 16 * i;
+    key[i] = e < E ? select_key(s[i], e) : 0;  // 0: below every real key
+  }
+  uint64_t mine = 0, top = 0;  // lane r keeps the r-th pick; top is the first
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) best = key[i] > best ? key[i] : best;
+    best = row16_max_u64(best);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (key[i] == best) key[i] = 0;
+    if (r == j) mine = best;
+    if (j == 0) top = best;
+  }
+  const float smax = key_score(top);
+  float w = 0.0f;
+  const float sj = key_score(mine);
+  if (gate == MOE_GATE_SOFTMAX) {
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (r + 16 * i < E) part += expf((s[i] - smax) * inv_temp);
+    const float denom = row16_sum(part);
+    w = expf((sj - smax) * inv_temp) / denom;
+  } else {
+    w = 1.0f / (1.0f + expf(-sj));
+  }
+  // threshold on the gate value before renormalisation (min_prob 0: off)
+  const bool keep = !(min_prob > 0.0f) || w > min_prob;
+  if (!keep) w = 0.0f;
+  if (renorm) {
+    const float tot = row16_sum(r < k ? w : 0.0f);
+    w = tot > 0.0f ? w / tot : 0.0f;
+  }
+  if (valid && r < k) {
+    idx_row[r] = keep ? (int32_t)(~(uint32_t)mine) : -1;
+    w_row[r] = w;
+  }
+}
+
+// Four tokens per wave, one per 16-lane row (E <= 256, k <= 16).
+template <int EPL>
+__global__ void __launch_bounds__(256)
+    topk_gate16_kernel(const float* __restrict__ logits, const float* __restrict__ bias,
+                       int T, int E, int k, int gate, int renorm, float inv_temp,
+                       float min_prob, int32_t* __restrict__ topk_idx,
+                       float* __restrict__ topk_w) {
+  const int lane = lane_id();
+  const int t0 = __builtin_amdgcn_readfirstlane(
+      (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 4);
+  if (t0 >= T) return;
+  const int t = t0 + (lane >> 4), r = lane & 15;
+  const bool valid = t < T;
+  const float* lg = logits + (long long)(valid ? t : T - 1) * E;
+  float s[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = r + 16 * i;
+    s[i] = 0.0f;
+    if (e < E) s[i] = bias ? lg[e] + bias[e] : lg[e];
+  }
+  topk_token16<EPL>(s, E, k, gate, renorm, inv_temp, min_prob, valid,
+                    topk_idx + (long long)t * k, topk_w + (long long)t * k);
+}
+
+// One wave per token; EPL = experts per lane (lane l holds e = l + 64*i).
+template <int EPL>
+__global__ void __launch_bounds__(256)
+    topk_gate_kernel(const float* __restrict__ logits, const float* __restrict__ bias,
+                     int T, int E, int k, int gate, int renorm, float inv_temp,
+                     float min_prob, int32_t* __restrict__ topk_idx,
+                     float* __restrict__ topk_w) {
+  const int lane = lane_id();
+  const int t = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
+  if (t >= T) return;
+  const float* lg = logits + (long long)t * E;
+  float s[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    s[i] = 0.0f;
+    if (e < E) s[i] = bias ? lg[e] + bias[e] : lg[e];
+  }
+  topk_token<EPL>(s, E, k, gate, renorm, inv_temp, min_prob, topk_idx + (long long)t * k,
+                  topk_w + (long long)t * k);
 }
 
 // 8 consecutive activations -> float (one or two 16-byte loads).
@@ -290,24 +414,34 @@ __global__ void __launch_bounds__(NW * 64)
 }
 
 // Router projection for many experts and large batches (E a multiple of
-// 256): one workgroup per 64 tokens scores them against 256 experts, so
-// each activation row is read from memory once.  Copies are staged as in the
+// 256): one workgroup per 64 tokens scores them against 256 experts, so each
+// activation row is read from memory once.  Copies are staged as in the
 // expert GEMMs (128-byte rows to LDS with global_load_lds, XOR-swizzled
-// chunks), but with three stages and two in flight: this tile's copies are
-// 40 KB and its matrix work per 64-wide k step is a quarter of a 256x256
-// tile's, so with one stage in flight each k step would wait out a whole
-// copy round trip.  Four waves of 64 tokens x 64 experts (2 x 2 tiles of
-// v_mfma_f32_32x32x16), float32 scores.
-template <int DT>
+// chunks), in two rings: activations, which stream from HBM, six 8 KB slots
+// with five k-steps in flight; router weights, which every workgroup reads
+// in the same order and so hit in L2, three 32 KB slots with two in flight.
+// With one or two activation stages in flight the kernel was bound by the
+// HBM round trip: 16 KB per CU in flight at ~2 us is ~2 TB/s over the chip.
+// Four waves of 64 tokens x 64 experts (2 x 2 tiles of v_mfma_f32_32x32x16),
+// float32 scores.  With TOPK (E == 256: the workgroup holds every score of
+// its tokens), the scores also go through LDS to top-k gating in the same
+// kernel, one wave per token as in topk_gate_kernel.
+template <int DT, bool TOPK>
 __global__ void __launch_bounds__(256)
-    router_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-                      int T, int H, int E, float* __restrict__ logits) {
-  constexpr int BM = 64, BN = 256, ROWB = 128, NS = 3, NW = 4;
-  constexpr int A_BYTES = BM * ROWB, STAGE = (BM + BN) * ROWB;
-  constexpr int BPW = (BM + BN) / 8 / NW;  // 1 KB copies per wave and stage
-  constexpr int JA = BM / 8 / NW;          // the first JA of them are A rows
+    router_ring_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                       int T, int H, int E, float* __restrict__ logits,
+                       const float* __restrict__ bias, int k, int gate, int renorm,
+                       float inv_temp, float min_prob, int32_t* __restrict__ topk_idx,
+                       float* __restrict__ topk_w) {
+  constexpr int BM = 64, BN = 256, ROWB = 128, NW = 4;
+  constexpr int NA = 6, NB = 3;                      // ring slots
+  constexpr int A_STAGE = BM * ROWB, B_STAGE = BN * ROWB;
+  constexpr int B_OFS = NA * A_STAGE;
+  constexpr int JA = BM / 8 / NW, JB = BN / 8 / NW;  // 1 KB copies per wave and stage
+  constexpr int LPITCH = BN + 1;                     // score tile row pitch (floats)
+  static_assert(!TOPK || BM * LPITCH * 4 <= NA * A_STAGE + NB * B_STAGE, "score tile");
   typedef typename MfmaOp<DT>::V V;
-  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[NA * A_STAGE + NB * B_STAGE];
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -317,24 +451,18 @@ __global__ void __launch_bounds__(256)
   const int m0 = (int)blockIdx.x * BM, n0 = (int)blockIdx.y * BN;
   const char* a_tile = uniform_ptr((const char*)(x + (long long)m0 * H));
   const char* b_tile = uniform_ptr((const char*)(wr + (long long)n0 * H));
-  uint32_t voff[BPW];
-  int ldsoff[BPW];
+  // copy j of a wave fills rows 8 (wave + NW j) .. + 7 of a stage (1 KB)
+  uint32_t voffA[JA], voffB[JB];
 #pragma unroll
-  for (int j = 0; j < BPW; ++j) {
-    const int q = wave + NW * j;
-    if (j < JA) {
-      const int row = 8 * q + prow;
-      const int kc = pchunk ^ dma_swz(row);
-      const int grow = min(m0 + row, T - 1);
-      voff[j] = (uint32_t)(grow - m0) * (uint32_t)(H * 2) + (uint32_t)(kc * 16);
-      ldsoff[j] = q * 1024;
-    } else {
-      const int qb = q - BM / 8;
-      const int row = 8 * qb + prow;
-      const int kc = pchunk ^ dma_swz(row);
-      voff[j] = (uint32_t)row * (uint32_t)(H * 2) + (uint32_t)(kc * 16);
-      ldsoff[j] = A_BYTES + qb * 1024;
-    }
+  for (int j = 0; j < JA; ++j) {
+    const int row = 8 * (wave + NW * j) + prow;
+    const int grow = min(m0 + row, T - 1);
+    voffA[j] = (uint32_t)(grow - m0) * (uint32_t)(H * 2) + (uint32_t)((pchunk ^ dma_swz(row)) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < JB; ++j) {
+    const int row = 8 * (wave + NW * j) + prow;
+    voffB[j] = (uint32_t)row * (uint32_t)(H * 2) + (uint32_t)((pchunk ^ dma_swz(row)) * 16);
   }
   f32x16 acc[2][2];
 #pragma unroll
@@ -345,13 +473,17 @@ __global__ void __launch_bounds__(256)
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   const int nk = H / 64;
   const uint32_t lds0 = lds_addr(smem);
-#define MOE_RISSUE(st)                                                          \
+#define MOE_ISSUE_A(st)                                                         \
   do {                                                                          \
-    const uint32_t dst_ = lds0 + ((st) % NS) * STAGE;                           \
-    const char* ak_ = a_tile + (st) * ROWB;                                     \
-    const char* bk_ = b_tile + (st) * ROWB;                                     \
-    _Pragma("unroll") for (int j = 0; j < BPW; ++j)                             \
-      dma16(j < JA ? ak_ : bk_, voff[j], dst_ + ldsoff[j]);                     \
+    const uint32_t dst_ = lds0 + ((st) % NA) * A_STAGE;                         \
+    _Pragma("unroll") for (int j = 0; j < JA; ++j)                              \
+      dma16(a_tile + (st) * ROWB, voffA[j], dst_ + (wave + NW * j) * 1024);     \
+  } while (0)
+#define MOE_ISSUE_B(st)                                                         \
+  do {                                                                          \
+    const uint32_t dst_ = lds0 + B_OFS + ((st) % NB) * B_STAGE;                 \
+    _Pragma("unroll") for (int j = 0; j < JB; ++j)                              \
+      dma16(b_tile + (st) * ROWB, voffB[j], dst_ + (wave + NW * j) * 1024);     \
   } while (0)
 #define MOE_RREAD(As, Bs, s4, FA, FB)                                           \
   do {                                                                          \
@@ -361,20 +493,33 @@ __global__ void __launch_bounds__(256)
       FB[j] = *(const V*)((Bs) + (wave * 64 + j * 32 + lrow) * ROWB +           \
                           (((2 * (s4)) ^ sw_row) << 4));                        \
   } while (0)
-  MOE_RISSUE(0);
-  if (nk > 1) MOE_RISSUE(1);
+  // prologue: activation stages 0 .. NA-2, then weight stages 0 .. NB-2
+#pragma unroll
+  for (int st = 0; st < NA - 1; ++st)
+    if (st < nk) MOE_ISSUE_A(st);
+#pragma unroll
+  for (int st = 0; st < NB - 1; ++st)
+    if (st < nk) MOE_ISSUE_B(st);
   for (int kt = 0; kt < nk; ++kt) {
-    // stage kt landed (stage kt+1 may be in flight); after the barrier every
-    // wave's copies of it are visible and every wave is done with stage
-    // kt-1, whose buffer takes stage kt+2
-    if (kt + 1 < nk) wait_vmcnt<BPW>();
+    // Stage kt has landed once at most the copies issued after its weight
+    // stage are in flight: for kt = 0 the prologue's weight stage 1; later,
+    // the activation stage kt + NA - 2 and the weight stage kt + NB - 2
+    // issued in iteration kt - 1 (when they exist).  Its activation stage
+    // was issued before its weight stage.  The barrier then covers every
+    // wave's copies and frees the slots read in iteration kt - 1.
+    const int after = kt == 0 ? (nk > 1 ? JB : 0)
+                              : (kt + NA - 2 < nk ? JA : 0) + (kt + NB - 2 < nk ? JB : 0);
+    if (after == JA + JB) wait_vmcnt<JA + JB>();
+    else if (after == JB) wait_vmcnt<JB>();
+    else if (after == JA) wait_vmcnt<JA>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x7 << 4) | ((0x3F >> 4) << 14));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kt + 2 < nk) MOE_RISSUE(kt + 2);
-    const char* As = smem + (kt % NS) * STAGE;
-    const char* Bs = As + A_BYTES;
+    if (kt + NA - 1 < nk) MOE_ISSUE_A(kt + NA - 1);
+    if (kt + NB - 1 < nk) MOE_ISSUE_B(kt + NB - 1);
+    const char* As = smem + (kt % NA) * A_STAGE;
+    const char* Bs = smem + B_OFS + (kt % NB) * B_STAGE;
     V fa0[2], fb0[2], fa1[2], fb1[2];
     MOE_RREAD(As, Bs, 0, fa0, fb0);
 #pragma unroll
@@ -391,20 +536,45 @@ __global__ void __launch_bounds__(256)
         for (int j = 0; j < 2; ++j) acc[i][j] = MfmaOp<DT>::run(fa1[i], fb1[j], acc[i][j]);
     }
   }
-#undef MOE_RISSUE
+#undef MOE_ISSUE_A
+#undef MOE_ISSUE_B
 #undef MOE_RREAD
   // 32x32 result layout: lane l holds column l % 32, rows 8 * (v / 4) +
   // 4 * (l / 32) + v % 4
+  float* tile = (float*)smem;  // TOPK: the 64 x 256 scores, row pitch LPITCH
+  if (TOPK) __syncthreads();   // every wave is done reading the rings
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = m0 + i * 32 + (v >> 2) * 8 + khalf * 4 + (v & 3);
-        const int col = n0 + wave * 64 + j * 32 + lrow;
-        if (row < T) logits[(long long)row * E + col] = acc[i][j][v];
+        const int r = i * 32 + (v >> 2) * 8 + khalf * 4 + (v & 3);
+        const int c = wave * 64 + j * 32 + lrow;
+        if (m0 + r < T) logits[(long long)(m0 + r) * E + n0 + c] = acc[i][j][v];
+        if (TOPK) tile[r * LPITCH + c] = acc[i][j][v];
       }
+  if (!TOPK) return;
+  __syncthreads();
+  // top-k gating of the block's tokens: four per wave at a time, one per
+  // 16-lane row, as in topk_gate16_kernel
+  const int rr = lane & 15;
+  float bl[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) bl[i] = bias ? bias[rr + 16 * i] : 0.0f;
+  for (int r0 = 4 * wave; r0 < BM; r0 += 4 * NW) {
+    const int r = r0 + (lane >> 4);
+    const int t = m0 + r;
+    if (m0 + r0 >= T) break;
+    float sc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float l = tile[r * LPITCH + rr + 16 * i];
+      sc[i] = bias ? l + bl[i] : l;  // one float32 addition, as in topk_gate_kernel
+    }
+    topk_token16<16>(sc, BN, k, gate, renorm, inv_temp, min_prob, t < T,
+                     topk_idx + (long long)t * k, topk_w + (long long)t * k);
+  }
 }
 
 namespace {
@@ -433,19 +603,38 @@ int launch_router_mfma(const void* x, const void* wr, int T, int H, int E, float
 }
 
 template <int DT>
-int launch_router_dma(const void* x, const void* wr, int T, int H, int E, float* logits,
-                      hipStream_t s) {
+int launch_router_ring(const void* x, const void* wr, int T, int H, int E, float* logits,
+                       const float* bias, int k, int gate, int renorm, float inv_temp,
+                       float min_prob, int32_t* idx, float* w, bool topk, hipStream_t s) {
   // per-lane copy offsets are 32-bit: 256 rows of H values must span < 4 GiB
   if ((long long)256 * H * 2 >= (1ll << 32)) return MOE_ERR_UNSUPPORTED;
   const dim3 grid((T + 63) / 64, E / 256);
-  hipLaunchKernelGGL((router_dma_kernel<DT>), grid, dim3(256), 0, s, (const uint16_t*)x,
-                     (const uint16_t*)wr, T, H, E, logits);
+  if (topk)
+    hipLaunchKernelGGL((router_ring_kernel<DT, true>), grid, dim3(256), 0, s,
+                       (const uint16_t*)x, (const uint16_t*)wr, T, H, E, logits, bias, k, gate,
+                       renorm, inv_temp, min_prob, idx, w);
+  else
+    hipLaunchKernelGGL((router_ring_kernel<DT, false>), grid, dim3(256), 0, s,
+                       (const uint16_t*)x, (const uint16_t*)wr, T, H, E, logits, bias, k, gate,
+                       renorm, inv_temp, min_prob, idx, w);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 int launch_topk(const float* logits, const float* bias, int T, int E, int k,
                 int gate, int renorm, float inv_temp, float min_prob, int32_t* idx,
                 float* w, hipStream_t s) {
+  if (E <= 256 && k <= 16) {
+    // four tokens per wave, sixteen per block
+    const dim3 grid16((T + 15) / 16), block16(256);
+#define MOE_TOPK16(EPL)                                                              \
+  hipLaunchKernelGGL((topk_gate16_kernel<EPL>), grid16, block16, 0, s, logits, bias, T, E, \
+                     k, gate, renorm, inv_temp, min_prob, idx, w)
+    if (E <= 64) MOE_TOPK16(4);
+    else if (E <= 128) MOE_TOPK16(8);
+    else MOE_TOPK16(16);
+#undef MOE_TOPK16
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  }
   const dim3 grid((T + 3) / 4), block(256);
 #define MOE_TOPK(EPL)                                                         \
   hipLaunchKernelGGL((topk_gate_kernel<EPL>), grid, block, 0, s, logits, bias, \
@@ -474,9 +663,17 @@ int route_impl(const void* x, const void* w_router, int act_dtype, const float* 
     const bool mfma = act_dtype != MOE_DTYPE_F32 && E >= 128 && E % 128 == 0 &&
                       H % 64 == 0 && T >= 1024;
     if (mfma && E % 256 == 0) {
+      // E == 256: one workgroup holds all of a token's scores, so top-k
+      // gating (k <= 16) runs in the same kernel
+      const bool fuse = E == 256 && k <= 16;
       st = act_dtype == MOE_DTYPE_F16
-               ? launch_router_dma<MOE_DTYPE_F16>(x, w_router, T, H, E, logits, s)
-               : launch_router_dma<MOE_DTYPE_BF16>(x, w_router, T, H, E, logits, s);
+               ? launch_router_ring<MOE_DTYPE_F16>(x, w_router, T, H, E, logits, bias, k, gate,
+                                                   renorm, inv_temp, min_prob, topk_idx,
+                                                   topk_w, fuse, s)
+               : launch_router_ring<MOE_DTYPE_BF16>(x, w_router, T, H, E, logits, bias, k, gate,
+                                                    renorm, inv_temp, min_prob, topk_idx,
+                                                    topk_w, fuse, s);
+      if (st != MOE_OK || fuse) return st;
     } else if (mfma) {
       GemmArgs a{};
       a.A = x;

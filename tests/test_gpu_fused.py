@@ -1,6 +1,13 @@
 """The fused dispatch -> GEMM-1 -> GEMM-2 -> combine kernel against the
-unfused path without the k-split workspace (same tiles and accumulation
-order: bit-identical results) and against the oracle at full size."""
+unfused path without the k-split workspace and against the oracle.
+
+Where the unfused GEMMs use the same tile as the fused kernel (at least 49
+rows per local expert on average), the two paths run the same tiles in the
+same accumulation order and must agree bit for bit.  With fewer rows the
+unfused GEMMs take the 32-row tile on 32x32x16 MFMAs, whose float32 sums can
+differ in the last bit from the fused kernel's 16x16x32 tiles; a 16-bit
+rounding of h can then land one unit apart, so those cases are compared
+within one unit in the last place (and against the oracle)."""
 
 import pytest
 import torch
@@ -22,6 +29,27 @@ def _fused_ws_ok(lay):
     assert lay.fused_status() == 0, "fused kernel reported a wait timeout"
 
 
+def _same_tiles(cfg):
+    """The unfused GEMMs use the fused kernel's tile (not the few-rows one)."""
+    e_loc = cfg.e_end - cfg.e_begin
+    return cfg.T * min(cfg.k, e_loc) / max(e_loc, 1) > 48
+
+
+def _ulp_close(x, y, what):
+    """Equal, or apart by at most one unit in the last place of the 16-bit
+    format, element by element."""
+    if torch.equal(x, y):
+        return
+    xf, yf = x.float(), y.float()
+    ulp = torch.where(xf.abs() > 0, torch.ldexp(torch.ones_like(xf),
+                                               torch.frexp(xf.abs())[1] - 11),
+                      torch.zeros_like(xf))      # fp16: 10 fraction bits
+    if x.dtype == torch.bfloat16:
+        ulp = ulp * 8                            # bf16: 7 fraction bits
+    bad = (xf - yf).abs() > ulp + 1e-30
+    assert not bool(bad.any()), f"{what}: {int(bad.sum())} elements more than 1 ulp apart"
+
+
 def _compare(cfg, a, b):
     r0 = int(a.offsets[cfg.e_begin])
     r1 = int(a.offsets[cfg.e_end])
@@ -29,9 +57,20 @@ def _compare(cfg, a, b):
         assert torch.equal(getattr(a, n), getattr(b, n)), n
     n_kept = int(a.offsets[-1])    # row_token past the kept picks is not written
     assert torch.equal(a.row_token[:n_kept], b.row_token[:n_kept])
-    assert torch.equal(a.out, b.out), "out differs from the unfused path"
-    assert torch.equal(a.y_perm[r0:r1], b.y_perm[r0:r1])
-    assert torch.equal(a.h[: r1 - r0], b.h[: r1 - r0])
+    if _same_tiles(cfg):
+        assert torch.equal(a.out, b.out), "out differs from the unfused path"
+        assert torch.equal(a.y_perm[r0:r1], b.y_perm[r0:r1])
+        assert torch.equal(a.h[: r1 - r0], b.h[: r1 - r0])
+        return
+    _ulp_close(a.h[: r1 - r0], b.h[: r1 - r0], "h")
+    # y and out inherit an h difference through a dot product: pooled and
+    # per row within 1e-3 (far inside the 16-bit tolerance against the oracle)
+    from tests.harness import assert_close
+    from oracle import moe_oracle as O
+    from oracle.torch_io import stored
+    for n, x, y in [("y_perm", a.y_perm[r0:r1], b.y_perm[r0:r1]), ("out", a.out, b.out)]:
+        assert_close(O.decode(stored(x), cfg.act_dtype), O.decode(stored(y), cfg.act_dtype),
+                     1e-3, n)
 
 
 @pytest.mark.parametrize("cfg", FUSED_SMALL, ids=[c.name for c in FUSED_SMALL])
