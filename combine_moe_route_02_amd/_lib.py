@@ -16,6 +16,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_ERR_TOO_LARGE = -5
+NOALLOC_SCRATCH_BYTES = 1 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 DTYPE_F32, DTYPE_F16, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2, 3
 GATE_SOFTMAX, GATE_SIGMOID = 0, 1
 ACT_SWIGLU, ACT_GELU = 0, 1
@@ -23,7 +25,7 @@ WS_DISPATCH, WS_FFN, WS_FUSED = 0, 1, 2
 # byte offset of moe_layer_fused's status word in its workspace (include/moe.h)
 FUSED_STATUS_BYTE = 32
 
-EXPORTS = ["moe_route", "moe_dispatch", "moe_dispatch_fp8", "moe_expert_ffn",
+EXPORTS = ["moe_route", "moe_dispatch", "moe_dispatch_noalloc", "moe_dispatch_fp8", "moe_expert_ffn",
            "moe_expert_ffn_up", "moe_expert_ffn_up_fp8", "moe_expert_ffn_down",
            "moe_combine", "moe_layer_fused", "moe_place_experts", "moe_expert_load_stats",
            "moe_workspace_bytes", "moe_status_string"]
@@ -41,6 +43,7 @@ P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
     "moe_route": [P, P, I, P, I, I, I, I, I, I, F, F, P, P, P, P],
     "moe_dispatch": [P, I, P, I, I, I, I, I, I, P, P, P, P, P, P, SZ, P],
+    "moe_dispatch_noalloc": [P, I, P, I, I, I, I, I, I, P, P, P, P, P, P],
     "moe_dispatch_fp8": [P, I, P, I, I, I, I, I, I, P, P, P, P, P, P, P, SZ, P],
     "moe_expert_ffn_up_fp8": [P, P, P, I, I, I, I, I, I, P, P, P, P],
     "moe_expert_ffn": [P, P, I, I, I, I, I, I, I, P, P, P, P, I, P, P, P, SZ, P],
@@ -112,6 +115,17 @@ def moe_dispatch(x, topk_idx, E, e_begin, e_end, counts, offsets, slot_of, row_t
         ptr(x), DTYPE_OF[x.dtype], ptr(topk_idx), T, H, E, k, e_begin, e_end,
         ptr(counts), ptr(offsets), ptr(slot_of), ptr(row_token), ptr(x_perm),
         ptr(ws), ws.numel() * ws.element_size(), stream_handle(stream)))
+
+
+def moe_dispatch_noalloc(x, topk_idx, E, e_begin, e_end, counts, offsets, slot_of,
+                         row_token, x_perm, stream=None):
+    """moe_dispatch with the library's fixed scratch as its workspace."""
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    check("moe_dispatch_noalloc", lib().moe_dispatch_noalloc(
+        ptr(x), DTYPE_OF[x.dtype], ptr(topk_idx), T, H, E, k, e_begin, e_end,
+        ptr(counts), ptr(offsets), ptr(slot_of), ptr(row_token), ptr(x_perm),
+        stream_handle(stream)))
 
 
 def moe_dispatch_fp8(x, topk_idx, E, e_begin, e_end, counts, offsets, slot_of, row_token,

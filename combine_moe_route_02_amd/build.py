@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
 SOURCES = ["api.hip", "route.hip", "dispatch.hip", "gemm.hip", "combine.hip",
-           "fused.hip", "placement.hip"]
+           "fused.hip", "placement.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",

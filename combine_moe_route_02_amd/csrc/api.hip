@@ -321,6 +321,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported dtype or shape";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "kernel launch failed";
+    case MOE_ERR_TOO_LARGE: return "sizes exceed the fixed internal scratch";
   }
   return "unknown status";
 }

@@ -51,7 +51,8 @@ enum moe_status {
   MOE_ERR_ARG = -1,          /* null pointer, bad size or range            */
   MOE_ERR_UNSUPPORTED = -2,  /* valid but not implemented (dtype, shape)   */
   MOE_ERR_WORKSPACE = -3,    /* workspace missing or too small             */
-  MOE_ERR_HIP = -4           /* a kernel launch failed                     */
+  MOE_ERR_HIP = -4,          /* a kernel launch failed                     */
+  MOE_ERR_TOO_LARGE = -5     /* sizes exceed a fixed internal scratch      */
 };
 
 enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_F16 = 1, MOE_DTYPE_BF16 = 2,
@@ -132,6 +133,29 @@ int moe_dispatch(const void* x, int act_dtype, const int32_t* topk_idx,
                  int32_t* counts, int32_t* offsets, int32_t* slot_of,
                  int32_t* row_token, void* x_perm, void* ws, size_t ws_bytes,
                  hipStream_t stream);
+
+/*
+ * moe_dispatch_noalloc - moe_dispatch without a workspace argument.
+ *
+ * For callers that cannot allocate device memory: code under stream capture,
+ * tight serving loops, harnesses that forbid allocation.  Arguments, layouts,
+ * results and validation are those of moe_dispatch; the workspace is instead
+ * a fixed array of MOE_NOALLOC_SCRATCH_BYTES bytes inside the library (one
+ * per GPU, held from the library's load until the process ends).  Nothing is
+ * allocated or freed by the call.  The first call on a device looks up that
+ * device's copy of the array (hipGetSymbolAddress; MOE_ERR_HIP if that
+ * fails).  Sizes whose workspace (moe_workspace_bytes(MOE_WS_DISPATCH, ...)
+ * = 8 * E * ceil(T / 256) bytes) exceeds the array return MOE_ERR_TOO_LARGE
+ * before anything is launched.  Every call on one GPU shares that GPU's
+ * array: calls that may overlap on one GPU (different streams without an
+ * ordering between them) race and must not be issued; calls ordered on one
+ * stream are safe.  Its contents need no clearing between calls.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (1u << 20)
+int moe_dispatch_noalloc(const void* x, int act_dtype, const int32_t* topk_idx,
+                         int T, int H, int E, int k, int e_begin, int e_end,
+                         int32_t* counts, int32_t* offsets, int32_t* slot_of,
+                         int32_t* row_token, void* x_perm, hipStream_t stream);
 
 /*
  * moe_dispatch_fp8 - moe_dispatch with the gathered rows sent in 8 bits.

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings():
     lib = L.lib()
     assert lib.moe_status_string(0) == b"ok"
-    for code in (-1, -2, -3, -4):
+    for code in (-1, -2, -3, -4, -5):
         assert lib.moe_status_string(code) not in (b"ok", b"unknown status")
 
 
@@ -237,3 +237,24 @@ def test_misaligned_row_buffers_are_rejected():
                                    0, 8, 0, w13, w2, h, y, out, FAKE, 1 << 30, None)
     for kw in ("x", "w13", "w2", "h", "y", "out"):
         assert fused(**{kw: ODD}) == L.MOE_ERR_ARG, kw
+
+
+def test_noalloc_dispatch_validation():
+    """The allocation-free dispatch validates like moe_dispatch and rejects
+    sizes whose workspace exceeds its fixed scratch, before any launch."""
+    lib = L.lib()
+    f = lib.moe_dispatch_noalloc
+    args = lambda T, H, E, k, e0, e1, dt=L.DTYPE_BF16, x=FAKE: (
+        x, dt, FAKE, T, H, E, k, e0, e1, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert f(*args(10, 64, 8, 2, 0, 8, dt=9)) == L.MOE_ERR_UNSUPPORTED
+    assert f(*args(10, 64, 8, 9, 0, 8)) == L.MOE_ERR_ARG
+    assert f(*args(10, 64, 8, 2, 5, 3)) == L.MOE_ERR_ARG
+    assert f(*args(10, 12, 8, 2, 0, 8)) == L.MOE_ERR_ARG          # 24-byte rows
+    assert f(*args(10, 64, 8, 2, 0, 8, x=ctypes.c_void_p(0x1004))) == L.MOE_ERR_ARG
+    # 8 * E * ceil(T / 256) bytes must fit the scratch: E = 1024 fits up to
+    # 128 tiles of 256 tokens
+    assert lib.moe_workspace_bytes(L.WS_DISPATCH, 128 * 256, 64, 1024, 8, 128) == \
+        L.NOALLOC_SCRATCH_BYTES
+    assert f(*args(128 * 256 + 1, 64, 1024, 8, 0, 8)) == L.MOE_ERR_TOO_LARGE
+    assert f(*args(1 << 20, 64, 256, 8, 0, 32)) == L.MOE_ERR_TOO_LARGE
+    assert lib.moe_status_string(L.MOE_ERR_TOO_LARGE) == b"sizes exceed the fixed internal scratch"
