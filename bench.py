@@ -65,6 +65,14 @@ def parse():
                          "--calib-copy-mib run into the per-launch HBM traffic summary")
     ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "OUT"),
                     help="turn a rocprofv3 --kernel-trace --stats CSV into a text summary")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("PMC_CSV", "OUT"),
+                    help="turn a rocprofv3 --pmc CSV (any SQ/GRBM counters) into "
+                         "per-kernel medians per dispatch, with MFMA busy and wait "
+                         "fractions when their counters are present")
+    ap.add_argument("--dense-gemm", action="store_true",
+                    help="time the library's GEMM (moe_expert_ffn_down, one expert) "
+                         "and hipBLASLt (torch.matmul) on the dense bf16 product "
+                         "4096 x 28672 x 4096, and print one JSON line")
     ap.add_argument("--fused", action="store_true",
                     help="time the fused dispatch->GEMM->combine kernel instead of "
                          "the four separate calls")
@@ -155,6 +163,11 @@ def main():
     if args.pmc_summary:
         return pmc_summary(*args.pmc_summary, calib_mib=args.calib_copy_mib or 1024,
                            workload=args.config, extra="--fused" if args.fused else "")
+    if args.counter_summary:
+        return counter_summary(*args.counter_summary, workload=args.config,
+                               dense=args.dense_gemm, extra="--fused" if args.fused else "")
+    if args.dense_gemm:
+        return dense_gemm(args)
     if args.stats_summary:
         return stats_summary(*args.stats_summary, workload=args.config,
                              extra="--fused" if args.fused else "")
@@ -570,6 +583,114 @@ def pmc_summary(fetch_csv, write_csv, out_path, calib_mib, workload, extra=""):
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+N_CU = 256   # MI355X compute units (4 SIMDs each)
+N_XCD = 8
+
+
+def counter_summary(pmc_csv, out_path, workload="c4", dense=False, extra=""):
+    """Per-kernel medians of every counter in one rocprofv3 --pmc CSV.
+    SQ_VALU_MFMA_BUSY_CYCLES is summed over the 1024 SIMDs (a dense 16-bit
+    product of F flops reads F / 1024: one SIMD retires 1024 bf16 flops per
+    busy cycle) and GRBM_GUI_ACTIVE over the 8 XCDs, so MFMA busy =
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 * 1024): the share of
+    SIMD cycles, while the kernel ran, in which a matrix core was busy
+    (padding rows of ragged tiles included).  The clock is GRBM_GUI_ACTIVE / 8
+    over the dispatch's duration.  Wait share = SQ_WAIT_ANY / SQ_WAVE_CYCLES:
+    the share of resident-wave cycles spent waiting on anything (memory
+    counters, barriers, dependencies)."""
+    import numpy as np
+    rows = _counter_rows(pmc_csv)
+    counters = sorted({r["Counter_Name"] for r in rows})
+    per = {}
+    for c in counters:
+        for k, v in _per_kernel(rows, c).items():
+            per.setdefault(k, {})[c] = v
+
+    def keep(name):
+        return name.startswith(("void moe::", "moe::")) or "Cijk" in name
+    if dense:
+        cmd = (f"python3 $R/bench.py --dense-gemm --steps 3 --warmup 1")
+        what = "dense bf16 4096 x 28672 x 4096: moe_expert_ffn_down (one expert) and hipBLASLt"
+    else:
+        cmd = (f"python3 $R/bench.py --config {workload} --steps 3 --warmup 1 "
+               f"--no-cpu-baseline {extra}").rstrip()
+        what = f"workload {workload}"
+    lines = [f"# rocprofv3 --pmc counters per kernel dispatch (median over dispatches), {what}",
+             "# command (from /tmp, TMPDIR=/tmp, R = repository root):",
+             f"#   rocprofv3 --pmc {' '.join(counters)} -f csv -d <dir> -o pmc -- {cmd}",
+             f"#   python3 $R/bench.py {'--dense-gemm' if dense else '--config ' + workload} "
+             f"{extra} --counter-summary <dir>/pmc_counter_collection.csv <out>".replace("  ", " "),
+             "# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs * 1024 SIMDs); "
+             "clock = GRBM_GUI_ACTIVE / 8 / dispatch duration; "
+             "wait_share = SQ_WAIT_ANY / SQ_WAVE_CYCLES"]
+    dur = {}
+    for r in rows:
+        if r["Counter_Name"] == counters[0]:
+            dur.setdefault(r["Kernel_Name"], []).append(
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    for k in sorted(per, key=lambda n: n):
+        if not keep(k):
+            continue
+        med = {c: float(np.median(v)) for c, v in per[k].items()}
+        n = max(len(v) for v in per[k].values())
+        parts = [f"{c} {med[c]:.4g}" for c in counters if c in med]
+        d_ns = float(np.median(dur[k])) if k in dur else 0.0
+        parts.append(f"duration_ns {d_ns:.0f}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in med and med.get("GRBM_GUI_ACTIVE"):
+            cyc = med["GRBM_GUI_ACTIVE"] / N_XCD
+            parts.append(f"mfma_busy {med['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * N_CU * 4):.3f}")
+            if d_ns >= 1e5:  # too coarse for short dispatches
+                parts.append(f"clock_ghz {cyc / d_ns:.2f}")
+        if "SQ_WAIT_ANY" in med and med.get("SQ_WAVE_CYCLES"):
+            parts.append(f"wait_share {med['SQ_WAIT_ANY'] / med['SQ_WAVE_CYCLES']:.3f}")
+        lines.append(f"{k[:110]}")
+        lines.append(f"    dispatches {n}: " + ", ".join(parts))
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def dense_gemm(args):
+    """The library's GEMM and hipBLASLt on one dense bf16 product."""
+    import torch
+    from combine_moe_route_02_amd import _lib as L
+    L.lib()
+    dev = torch.device("cuda:0")
+    M, N, K = 4096, 28672, 4096
+    g = torch.Generator(device="cpu").manual_seed(7)
+    h = torch.randn(M, K, generator=g).to(torch.bfloat16).to(dev)
+    w2 = (torch.randn(1, N, K, generator=g) / K ** 0.5).to(torch.bfloat16).to(dev)
+    offsets = torch.tensor([0, M], dtype=torch.int32, device=dev)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    wt = w2[0]
+    ours = lambda: L.moe_expert_ffn_down(offsets, N, K, 0, 1, M, w2, None, h, y)
+    blas = lambda: torch.matmul(h, wt.T)
+
+    def timed(fn):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ev)
+        return t[len(t) // 2]
+    t_ours, t_blas = timed(ours), timed(blas)
+    ref = blas().float()
+    err = ((y.float() - ref).norm() / ref.norm()).item()
+    fl = 2.0 * M * N * K
+    res = {"shape": [M, N, K], "dtype": "bf16", "steps": args.steps,
+           "ours_ms": round(t_ours, 4), "hipblaslt_ms": round(t_blas, 4),
+           "ours_frac_mfma": round(fl / t_ours / 1e9 / PEAK_MFMA_TFLOPS, 4),
+           "hipblaslt_frac_mfma": round(fl / t_blas / 1e9 / PEAK_MFMA_TFLOPS, 4),
+           "rel_l2_vs_hipblaslt": err}
+    print(json.dumps(res), flush=True)
 
 
 def stats_summary(stats_csv, out_path, workload="c2", extra=""):

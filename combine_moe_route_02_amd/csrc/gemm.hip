@@ -821,6 +821,12 @@ inline bool few_rows(const GemmArgs& a, int max_rows) {
   return (double)rows / (groups > 0 ? groups : 1) <= 48.0;
 }
 
+// m-tiles per band of the expert-band tile order (weight tiles shared by a
+// band's m-tiles close together in time)
+#ifndef MOE_BAND_GM
+#define MOE_BAND_GM 8
+#endif
+
 template <int DT, int WK, int EPI>
 int pick_tile(GemmArgs a, int max_rows, hipStream_t s) {
   if constexpr (EPI == EPI_F32) {
@@ -835,8 +841,8 @@ int pick_tile(GemmArgs a, int max_rows, hipStream_t s) {
     }
     if constexpr (WK == W_SAME) {
       if (choose_bm<WK>(a, max_rows) == 256)
-        return run_dma<DT, EPI, 256, 256, 2, 2>(a, max_rows, 8, s);
-      return run_dma<DT, EPI, 128, 256, 2, 2>(a, max_rows, 8, s);
+        return run_dma<DT, EPI, 256, 256, 2, 2>(a, max_rows, MOE_BAND_GM, s);
+      return run_dma<DT, EPI, 128, 256, 2, 2>(a, max_rows, MOE_BAND_GM, s);
     } else {
       return run_mfma<DT, WK, EPI, 128, 256, 2, 2>(a, max_rows, 8, s);
     }

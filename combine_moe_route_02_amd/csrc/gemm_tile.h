@@ -223,6 +223,14 @@ __device__ __forceinline__ float gelu_erf16(float a) {
 // 16 lanes x 16 B (64 banks) per cycle.
 __device__ __forceinline__ int dma_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
+// L2 prefetch distance of the weight rows (k-steps), and a switch for it.
+#ifndef MOE_PFD
+#define MOE_PFD 4
+#endif
+#ifndef MOE_PF_ON
+#define MOE_PF_ON 1
+#endif
+
 #ifndef MOE_SKEW
 #define MOE_SKEW(nt, nk) ((((nt) & 7) * 2) % (nk))
 #endif
@@ -345,7 +353,8 @@ struct DmaTile {
   // line.  Activation rows are not prefetched: a band's workgroups share
   // them and keep them in L2, while prefetching them too evicts weight lines
   // before their copies (GEMM-1 and GEMM-2 5-15% slower measured with both).
-  static constexpr int PFD = 4;
+  static constexpr int PFD = MOE_PFD;
+  static constexpr bool PF_ON = MOE_PF_ON != 0;
   static constexpr int NPF = (BN + 64 * NW - 1) / (64 * NW);  // prefetches per wave and k-step
   static constexpr int PF_OFS = NS * STAGE;                         // scratch slots
   static constexpr int SMEM = NS * STAGE + NW * 256;
@@ -550,12 +559,14 @@ do {                                                                            
 #define MOE_PREFETCH(st)                                                           \
 do {                                                                             \
     const uint32_t pdst_ = lds0 + PF_OFS + wave * 256;                             \
-    _Pragma("unroll") for (int i = 0; i < NPF; ++i)                                \
-      prefetch4(b_tile + MOE_KOFS(st), pfoff[i], pdst_);                           \
+    if (PF_ON) {                                                                   \
+      _Pragma("unroll") for (int i = 0; i < NPF; ++i)                              \
+        prefetch4(b_tile + MOE_KOFS(st), pfoff[i], pdst_);                         \
+    }                                                                              \
 } while (0)
 // Wait until at most n_pf prefetch groups (issued after the stage's copies)
 // are in flight.
-#define MOE_WAIT_STAGE(n_pf) wait_vmcnt_groups<0, NPF, PFD - 2>(n_pf)
+#define MOE_WAIT_STAGE(n_pf) wait_vmcnt_groups<0, NPF, PFD - 2>(PF_ON ? (n_pf) : 0)
 // sched_barrier(0) keeps each phase's LDS reads ahead of the MFMAs that
 // overlap them (the scheduler would otherwise sink each read to its use).
 #define MOE_PHASE() __builtin_amdgcn_sched_barrier(0)
@@ -570,7 +581,7 @@ do {                                                                            
       if (s_ < nk) MOE_PREFETCH(s_);
     // stage 0 landed; stage 1 and the npf0 prefetch groups issued after it
     // may be in flight
-    const int npf0 = nk > 2 ? (nk < PFD ? nk : PFD) - 2 : 0;
+    const int npf0 = PF_ON && nk > 2 ? (nk < PFD ? nk : PFD) - 2 : 0;
     if (nk <= 1) wait_vmcnt<0>();
     else wait_vmcnt_groups<BPW, NPF, PFD - 2>(npf0);
     __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x7 << 4) | ((0x3F >> 4) << 14));
@@ -663,7 +674,7 @@ do {                                                                            
 #undef MOE_WAIT_STAGE
 #undef MOE_KOFS
 
-    if (nxt_g >= 0) {
+    if (PF_ON && nxt_g >= 0) {
       const char* b2 = uniform_ptr((const char*)p.B + (long long)nxt_g * p.strideB * 2);
       const int nk2 = p.K / BK;
       const int skew2 = MOE_SKEW(nxt_nt, nk2);
