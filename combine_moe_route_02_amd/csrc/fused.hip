@@ -108,6 +108,53 @@ __device__ __forceinline__ void slice(int total, int q, int& lo, int& len) {
   len = (int)(b - a);
 }
 
+// One token's output row by one wave: out = sum over picks j < k of
+// w_j * y_perm[row_j], in pick order, in float32, rounded once (as
+// moe_combine); a dropped pick (row -1) adds nothing.  KM >= k picks are
+// loaded for U 16-byte chunks per lane at a time with no condition on any
+// load (picks past k and dropped picks load row 0, a lane past the row end
+// loads its last chunk; neither is used), so all KM x U loads are in flight
+// together: with one wave per SIMD in this kernel, that is what keeps HBM
+// busy (one chunk per pick at a time ran the fused combine at under half
+// the standalone combine's rate).  Each row is read once: non-temporal loads.
+template <int DT, int KM>
+__device__ __forceinline__ void combine_row(const uint4* __restrict__ y_perm,
+                                            const long long (&rj)[8], const float (&wj)[8],
+                                            int k, int nch, uint4* __restrict__ dst,
+                                            int lane) {
+  constexpr int U = 32 / KM;
+  for (int cb = 0; cb < nch; cb += 64 * U) {
+    uint4 qv[U][KM];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = min(cb + 64 * u + lane, nch - 1);
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        const long long r = j < k && rj[j] >= 0 ? rj[j] : 0;
+        qv[u][j] = __builtin_bit_cast(
+            uint4, __builtin_nontemporal_load((const u32x4*)&y_perm[r + c]));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        if (j < k && rj[j] >= 0) {
+          float v[8];
+          unpack8<DT>(qv[u][j], v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = fmaf(wj[j], v[e], acc[e]);
+        }
+      }
+      const int c = cb + 64 * u + lane;
+      if (c < nch) dst[c] = pack8<DT>(acc);
+    }
+  }
+}
+
 template <int DT, int BM, int BN, int WM, int WN>
 __global__ void __launch_bounds__(WM * WN * 64) fused_layer_kernel(FusedArgs f) {
   typedef DmaTile<DT, EPI_SWIGLU, BM, BN, WM, WN> T1;
@@ -135,6 +182,17 @@ __global__ void __launch_bounds__(WM * WN * 64) fused_layer_kernel(FusedArgs f) 
   const int lane = (int)threadIdx.x & 63;
   const int wave = (int)threadIdx.x >> 6;
   const int e0 = f.g1.e_begin, ng = f.g1.n_groups;
+  // When this queue's GEMM-2 slice starts inside a band that began in the
+  // previous queue's slice, the band's m-tiles got part of their GEMM-1
+  // tiles at the end of the previous queue's GEMM-1 work, so they are the
+  // last to be ready; the rest of the slice's bands finished GEMM-1 in this
+  // queue, in order.  Their items go first and the straddling band's last.
+  int rot2 = 0;
+  if (len2 > 0) {
+    int b0, b1;
+    band_bounds(f.g2, s_pre, lo2, nt2, f.g2.gm, b0, b1);
+    if (b0 < lo2 && b1 - lo2 < len2) rot2 = b1 - lo2;
+  }
 
   for (;;) {
     if (threadIdx.x == 0) s_item = __hip_atomic_fetch_add(hdr + q, 1, __ATOMIC_RELAXED,
@@ -152,7 +210,8 @@ __global__ void __launch_bounds__(WM * WN * 64) fused_layer_kernel(FusedArgs f) 
     it -= len1;
     if (it < len2) {
       int mt, nt;
-      const TileInfo ti = band_tile<BM>(f.g2, s_pre, lo2 + it, nt2, f.g2.gm, mt, nt);
+      const int it2 = it + rot2 < len2 ? it + rot2 : it + rot2 - len2;
+      const TileInfo ti = band_tile<BM>(f.g2, s_pre, lo2 + it2, nt2, f.g2.gm, mt, nt);
       if (!block_wait(cnt1 + mt, nt1, err, &s_flag)) return;
       T2::run(f.g2, ti, nt, smem, nullptr);
       block_signal(cnt2 + mt);
@@ -161,7 +220,7 @@ __global__ void __launch_bounds__(WM * WN * 64) fused_layer_kernel(FusedArgs f) 
     it -= len2;
     if (it >= len3) return;
 
-    // Combine block: one wave per token, 16 tokens per wave.
+    // Combine block: one wave per token, kTokensPerItem / 4 tokens per wave.
     const int r_lo = f.g1.offsets[e0];
     const int r_hi = f.g1.offsets[e0 + ng];
     const int tb = (lo3 + it) * kTokensPerItem;
@@ -198,33 +257,19 @@ __global__ void __launch_bounds__(WM * WN * 64) fused_layer_kernel(FusedArgs f) 
       const float w = lane < f.k ? f.topk_w[(long long)t * f.k + lane] : 0.0f;
       uint4* dst = f.out + (long long)t * f.nch;
       if (f.k <= 8) {
-        // rows and weights in registers, all k loads of a chunk in flight
+        // rows and weights in scalar registers (lane j holds pick j), so
+        // every test on them is a uniform branch
         long long rj[8];
         float wj[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          rj[j] = (long long)__shfl(row, j < f.k ? j : 0, 64) * f.nch;
-          wj[j] = j < f.k ? __shfl(w, j, 64) : 0.0f;
+          rj[j] = (long long)__builtin_amdgcn_readlane(row, j < f.k ? j : 0) * f.nch;
+          wj[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
         }
-        for (int c = lane; c < f.nch; c += 64) {
-          uint4 qv[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (j < f.k && rj[j] >= 0) qv[j] = f.y_perm[rj[j] + c];
-          float acc[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            if (j < f.k && rj[j] >= 0) {
-              float v[8];
-              unpack8<DT>(qv[j], v);
-#pragma unroll
-              for (int e = 0; e < 8; ++e) acc[e] = fmaf(wj[j], v[e], acc[e]);
-            }
-          }
-          dst[c] = pack8<DT>(acc);
-        }
+        if (f.k <= 1) combine_row<DT, 1>(f.y_perm, rj, wj, f.k, f.nch, dst, lane);
+        else if (f.k <= 2) combine_row<DT, 2>(f.y_perm, rj, wj, f.k, f.nch, dst, lane);
+        else if (f.k <= 4) combine_row<DT, 4>(f.y_perm, rj, wj, f.k, f.nch, dst, lane);
+        else combine_row<DT, 8>(f.y_perm, rj, wj, f.k, f.nch, dst, lane);
         continue;
       }
       for (int c = lane; c < f.nch; c += 64) {

@@ -51,6 +51,29 @@ __device__ __forceinline__ int build_mtile_table(const GemmArgs& p, int* s_pre, 
   return carry;
 }
 
+// Tiles [b0, b1) of the expert-band order form the band that holds tile t
+// (the same bands as band_tile).
+__device__ __forceinline__ void band_bounds(const GemmArgs& p, const int* s_pre, int t,
+                                            int n_tiles, int gm, int& b0, int& b1) {
+  int g = 0;
+  if (p.offsets != nullptr) {
+    int lo = 0, hi = p.n_groups - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pre[mid] * n_tiles > t) hi = mid; else lo = mid + 1;
+    }
+    g = lo;
+  }
+  const int m_before = g > 0 ? s_pre[g - 1] : 0;
+  const int mt_g = s_pre[g] - m_before;
+  const int w = t - m_before * n_tiles;
+  const int full = mt_g / gm;
+  const int per_band = gm * n_tiles;
+  const int band = w / per_band;
+  b0 = m_before * n_tiles + (band < full ? band : full) * per_band;
+  b1 = band < full ? b0 + per_band : (m_before + mt_g) * n_tiles;
+}
+
 // Tile t of the expert-band order -> its m-tile, n-tile and rows.  The tiles
 // of one group (its m-tiles x all n-tiles) are consecutive, so every weight
 // tile of a group is used by all of that group's m-tiles close together in
