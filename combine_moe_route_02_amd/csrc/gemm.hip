@@ -27,7 +27,7 @@
 //
 // Epilogues: plain store in the activation dtype, SwiGLU (the B tile
 // interleaves 32-row groups of gate and up rows so a wave holds both halves
-// of the same h columns), exact-erf GELU, or float32 (router logits).
+// of the same h columns), or exact-erf GELU.
 // fp8 E4M3 weights are decoded and scaled by their 128x128 tile scale while
 // being staged to LDS as bf16.
 
@@ -250,11 +250,6 @@ __global__ void __launch_bounds__(WM * WN * 64)
           const int col = n0h + (wn * (TN / 2) + jp) * 32 + lrow;
           C[crow * p.ldc + col] = Act<DT>::store(h);
         }
-      } else if (EPI == EPI_F32) {
-        float* C = (float*)p.C;
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          C[crow * p.ldc + n0 + wn * WTN + j * 32 + lrow] = acc[i][j][v];
       } else {
         uint16_t* C = (uint16_t*)p.C;
 #pragma unroll
@@ -829,23 +824,16 @@ inline bool few_rows(const GemmArgs& a, int max_rows) {
 
 template <int DT, int WK, int EPI>
 int pick_tile(GemmArgs a, int max_rows, hipStream_t s) {
-  if constexpr (EPI == EPI_F32) {
-    // router logits: one n-tile of 256 experts reads each token row once
-    if (WK == W_SAME && a.Nb % 256 == 0) return run_dma<DT, EPI, 64, 256, 1, 4>(a, max_rows, 4, s);
-    if (WK == W_SAME) return run_dma<DT, EPI, 64, 128, 2, 2>(a, max_rows, 4, s);
-    return run_mfma<DT, WK, EPI, 64, 128, 2, 2>(a, max_rows, 4, s);
+  if (few_rows(a, max_rows)) {
+    if constexpr (WK == W_FP8 && DT == MOE_DTYPE_BF16) return run_fp8s<DT, EPI>(a, max_rows, s);
+    return run_mfma<DT, WK, EPI, 32, 256, 1, 4>(a, max_rows, 1, s);
+  }
+  if constexpr (WK == W_SAME) {
+    if (choose_bm<WK>(a, max_rows) == 256)
+      return run_dma<DT, EPI, 256, 256, 2, 2>(a, max_rows, MOE_BAND_GM, s);
+    return run_dma<DT, EPI, 128, 256, 2, 2>(a, max_rows, MOE_BAND_GM, s);
   } else {
-    if (few_rows(a, max_rows)) {
-      if constexpr (WK == W_FP8 && DT == MOE_DTYPE_BF16) return run_fp8s<DT, EPI>(a, max_rows, s);
-      return run_mfma<DT, WK, EPI, 32, 256, 1, 4>(a, max_rows, 1, s);
-    }
-    if constexpr (WK == W_SAME) {
-      if (choose_bm<WK>(a, max_rows) == 256)
-        return run_dma<DT, EPI, 256, 256, 2, 2>(a, max_rows, MOE_BAND_GM, s);
-      return run_dma<DT, EPI, 128, 256, 2, 2>(a, max_rows, MOE_BAND_GM, s);
-    } else {
-      return run_mfma<DT, WK, EPI, 128, 256, 2, 2>(a, max_rows, 8, s);
-    }
+    return run_mfma<DT, WK, EPI, 128, 256, 2, 2>(a, max_rows, 8, s);
   }
 }
 
@@ -866,7 +854,6 @@ int by_epi(int epi, GemmArgs a, int max_rows, hipStream_t s) {
     case EPI_STORE: return pick_tile<DT, WK, EPI_STORE>(a, max_rows, s);
     case EPI_SWIGLU: return pick_tile<DT, WK, EPI_SWIGLU>(a, max_rows, s);
     case EPI_GELU: return pick_tile<DT, WK, EPI_GELU>(a, max_rows, s);
-    case EPI_F32: return pick_tile<DT, WK, EPI_F32>(a, max_rows, s);
   }
   return MOE_ERR_ARG;
 }
@@ -889,7 +876,6 @@ int launch_grouped_gemm(int act_dtype, int w_dtype, int epi, GemmArgs a,
     if (w_dtype != MOE_DTYPE_F32) return MOE_ERR_UNSUPPORTED;
     switch (epi) {
       case EPI_STORE: return run_f32<EPI_STORE>(a, max_rows, stream);
-      case EPI_F32: return run_f32<EPI_STORE>(a, max_rows, stream);
       case EPI_SWIGLU: return run_f32<EPI_SWIGLU>(a, max_rows, stream);
       case EPI_GELU: return run_f32<EPI_GELU>(a, max_rows, stream);
     }
@@ -897,7 +883,7 @@ int launch_grouped_gemm(int act_dtype, int w_dtype, int epi, GemmArgs a,
   }
   if (act_dtype == MOE_DTYPE_BF16) {
     if (w_dtype == MOE_DTYPE_BF16) return by_epi<MOE_DTYPE_BF16, W_SAME>(epi, a, max_rows, stream);
-    if (w_dtype == MOE_DTYPE_FP8_E4M3 && epi != EPI_F32)
+    if (w_dtype == MOE_DTYPE_FP8_E4M3)
       return by_epi<MOE_DTYPE_BF16, W_FP8>(epi, a, max_rows, stream);
     return MOE_ERR_UNSUPPORTED;
   }

@@ -394,7 +394,7 @@ struct DmaTile {
   // the stage buffers, OPITCH bytes per row, 16-byte pieces of row r
   // swizzled by ochunk(r); OCPR pieces per row, ORPP rows per pass of the
   // block.
-  static constexpr int OES = EPI == EPI_F32 ? 4 : 2;
+  static constexpr int OES = 2;
   static constexpr int OCOLS = EPI == EPI_SWIGLU ? BN / 2 : BN;
   static constexpr int OPITCH = OCOLS * OES;
   static constexpr int OCPR = OPITCH / 16;
@@ -827,13 +827,9 @@ do {                                                                            
             for (int v = 0; v < NV; ++v) {
               const int orow = wm * WTM + i * MI + (MI == 32 ? (v >> 2) * 8 + (v & 3) : v) + rsub;
               float y = acc_read(acc[i][j][v]);
-              if (EPI == EPI_F32) {
-                *(float*)(smem + obyte(orow, ocol)) = y;
-              } else {
-                if (EPI == EPI_GELU) y = gelu_erf16(y);
-                *(uint16_t*)(smem + obyte(orow, ocol)) = Act<DT>::store(y);
-                if (EPI == EPI_GELU) __builtin_amdgcn_sched_barrier(0);
-              }
+              if (EPI == EPI_GELU) y = gelu_erf16(y);
+              *(uint16_t*)(smem + obyte(orow, ocol)) = Act<DT>::store(y);
+              if (EPI == EPI_GELU) __builtin_amdgcn_sched_barrier(0);
             }
           }
         }
@@ -900,14 +896,10 @@ do {                                                                            
           for (int v = 0; v < NV; ++v) {
             if (!ok[v]) continue;
             float y = acc_read(acc[i][j][v]);
-            if (EPI == EPI_F32) {
-              ((float*)p.C)[(long long)crow[v] * p.ldc + col] = y;
-            } else {
-              if (EPI == EPI_GELU) y = gelu_erf16(y);
-              ((uint16_t*)p.C)[(long long)crow[v] * p.ldc + col] = Act<DT>::store(y);
-              // erf is long: one value at a time keeps its temporaries few
-              if (EPI == EPI_GELU) __builtin_amdgcn_sched_barrier(0);
-            }
+            if (EPI == EPI_GELU) y = gelu_erf16(y);
+            ((uint16_t*)p.C)[(long long)crow[v] * p.ldc + col] = Act<DT>::store(y);
+            // erf is long: one value at a time keeps its temporaries few
+            if (EPI == EPI_GELU) __builtin_amdgcn_sched_barrier(0);
           }
         }
       }

@@ -5,7 +5,7 @@
 
 namespace moe {
 
-enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_GELU = 2, EPI_F32 = 3 };
+enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_GELU = 2 };
 
 // One grouped GEMM  C[r, n] = epi( sum_k A[r, k] * B_g[n', k] )  over the
 // row segments of groups g = 0..n_groups-1.

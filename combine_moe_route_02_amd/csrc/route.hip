@@ -13,8 +13,9 @@
 // Selection key.  s = logit + bias (one float32 add), -0.0 made +0.0, mapped
 // to an order-preserving uint32 and placed above the complement of the
 // expert index: the largest 64-bit key is the largest score and, among equal
-// scores, the lowest index.  One wave owns a token; k rounds of a wave-wide
-// uint64 max pick the experts in descending order.
+// scores, the lowest index.  A 16-lane row of a wave owns a token (E <= 256,
+// k <= 16; otherwise a whole wave does); k rounds of a uint64 max over the
+// row pick the experts in descending order.
 
 #include "gemm_tile.h"
 
@@ -413,170 +414,6 @@ __global__ void __launch_bounds__(NW * 64)
   }
 }
 
-// Router projection for many experts and large batches (E a multiple of
-// 256): one workgroup per 64 tokens scores them against 256 experts, so each
-// activation row is read from memory once.  Copies are staged as in the
-// expert GEMMs (128-byte rows to LDS with global_load_lds, XOR-swizzled
-// chunks), in two rings: activations, which stream from HBM, six 8 KB slots
-// with five k-steps in flight; router weights, which every workgroup reads
-// in the same order and so hit in L2, three 32 KB slots with two in flight.
-// With one or two activation stages in flight the kernel was bound by the
-// HBM round trip: 16 KB per CU in flight at ~2 us is ~2 TB/s over the chip.
-// Four waves of 64 tokens x 64 experts (2 x 2 tiles of v_mfma_f32_32x32x16),
-// float32 scores.  With TOPK (E == 256: the workgroup holds every score of
-// its tokens), the scores also go through LDS to top-k gating in the same
-// kernel, one wave per token as in topk_gate_kernel.
-template <int DT, bool TOPK>
-__global__ void __launch_bounds__(256)
-    router_ring_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-                       int T, int H, int E, float* __restrict__ logits,
-                       const float* __restrict__ bias, int k, int gate, int renorm,
-                       float inv_temp, float min_prob, int32_t* __restrict__ topk_idx,
-                       float* __restrict__ topk_w) {
-  constexpr int BM = 64, BN = 256, ROWB = 128, NW = 4;
-  constexpr int NA = 6, NB = 3;                      // ring slots
-  constexpr int A_STAGE = BM * ROWB, B_STAGE = BN * ROWB;
-  constexpr int B_OFS = NA * A_STAGE;
-  constexpr int JA = BM / 8 / NW, JB = BN / 8 / NW;  // 1 KB copies per wave and stage
-  constexpr int LPITCH = BN + 1;                     // score tile row pitch (floats)
-  static_assert(!TOPK || BM * LPITCH * 4 <= NA * A_STAGE + NB * B_STAGE, "score tile");
-  typedef typename MfmaOp<DT>::V V;
-  __shared__ __attribute__((aligned(1024))) char smem[NA * A_STAGE + NB * B_STAGE];
-  const int tid = (int)threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lrow = lane & 31, khalf = lane >> 5;
-  const int prow = lane >> 3, pchunk = lane & 7;
-  const int sw_row = dma_swz(lrow) ^ khalf;
-  const int m0 = (int)blockIdx.x * BM, n0 = (int)blockIdx.y * BN;
-  const char* a_tile = uniform_ptr((const char*)(x + (long long)m0 * H));
-  const char* b_tile = uniform_ptr((const char*)(wr + (long long)n0 * H));
-  // copy j of a wave fills rows 8 (wave + NW j) .. + 7 of a stage (1 KB)
-  uint32_t voffA[JA], voffB[JB];
-#pragma unroll
-  for (int j = 0; j < JA; ++j) {
-    const int row = 8 * (wave + NW * j) + prow;
-    const int grow = min(m0 + row, T - 1);
-    voffA[j] = (uint32_t)(grow - m0) * (uint32_t)(H * 2) + (uint32_t)((pchunk ^ dma_swz(row)) * 16);
-  }
-#pragma unroll
-  for (int j = 0; j < JB; ++j) {
-    const int row = 8 * (wave + NW * j) + prow;
-    voffB[j] = (uint32_t)row * (uint32_t)(H * 2) + (uint32_t)((pchunk ^ dma_swz(row)) * 16);
-  }
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-  const int nk = H / 64;
-  const uint32_t lds0 = lds_addr(smem);
-#define MOE_ISSUE_A(st)                                                         \
-  do {                                                                          \
-    const uint32_t dst_ = lds0 + ((st) % NA) * A_STAGE;                         \
-    _Pragma("unroll") for (int j = 0; j < JA; ++j)                              \
-      dma16(a_tile + (st) * ROWB, voffA[j], dst_ + (wave + NW * j) * 1024);     \
-  } while (0)
-#define MOE_ISSUE_B(st)                                                         \
-  do {                                                                          \
-    const uint32_t dst_ = lds0 + B_OFS + ((st) % NB) * B_STAGE;                 \
-    _Pragma("unroll") for (int j = 0; j < JB; ++j)                              \
-      dma16(b_tile + (st) * ROWB, voffB[j], dst_ + (wave + NW * j) * 1024);     \
-  } while (0)
-#define MOE_RREAD(As, Bs, s4, FA, FB)                                           \
-  do {                                                                          \
-    _Pragma("unroll") for (int i = 0; i < 2; ++i)                               \
-      FA[i] = *(const V*)((As) + (i * 32 + lrow) * ROWB + (((2 * (s4)) ^ sw_row) << 4)); \
-    _Pragma("unroll") for (int j = 0; j < 2; ++j)                               \
-      FB[j] = *(const V*)((Bs) + (wave * 64 + j * 32 + lrow) * ROWB +           \
-                          (((2 * (s4)) ^ sw_row) << 4));                        \
-  } while (0)
-  // prologue: activation stages 0 .. NA-2, then weight stages 0 .. NB-2
-#pragma unroll
-  for (int st = 0; st < NA - 1; ++st)
-    if (st < nk) MOE_ISSUE_A(st);
-#pragma unroll
-  for (int st = 0; st < NB - 1; ++st)
-    if (st < nk) MOE_ISSUE_B(st);
-  for (int kt = 0; kt < nk; ++kt) {
-    // Stage kt has landed once at most the copies issued after its weight
-    // stage are in flight: for kt = 0 the prologue's weight stage 1; later,
-    // the activation stage kt + NA - 2 and the weight stage kt + NB - 2
-    // issued in iteration kt - 1 (when they exist).  Its activation stage
-    // was issued before its weight stage.  The barrier then covers every
-    // wave's copies and frees the slots read in iteration kt - 1.
-    const int after = kt == 0 ? (nk > 1 ? JB : 0)
-                              : (kt + NA - 2 < nk ? JA : 0) + (kt + NB - 2 < nk ? JB : 0);
-    if (after == JA + JB) wait_vmcnt<JA + JB>();
-    else if (after == JB) wait_vmcnt<JB>();
-    else if (after == JA) wait_vmcnt<JA>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x7 << 4) | ((0x3F >> 4) << 14));
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (kt + NA - 1 < nk) MOE_ISSUE_A(kt + NA - 1);
-    if (kt + NB - 1 < nk) MOE_ISSUE_B(kt + NB - 1);
-    const char* As = smem + (kt % NA) * A_STAGE;
-    const char* Bs = smem + B_OFS + (kt % NB) * B_STAGE;
-    V fa0[2], fb0[2], fa1[2], fb1[2];
-    MOE_RREAD(As, Bs, 0, fa0, fb0);
-#pragma unroll
-    for (int s4 = 0; s4 < 4; s4 += 2) {
-      MOE_RREAD(As, Bs, s4 + 1, fa1, fb1);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = MfmaOp<DT>::run(fa0[i], fb0[j], acc[i][j]);
-      if (s4 + 2 < 4) MOE_RREAD(As, Bs, s4 + 2, fa0, fb0);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = MfmaOp<DT>::run(fa1[i], fb1[j], acc[i][j]);
-    }
-  }
-#undef MOE_ISSUE_A
-#undef MOE_ISSUE_B
-#undef MOE_RREAD
-  // 32x32 result layout: lane l holds column l % 32, rows 8 * (v / 4) +
-  // 4 * (l / 32) + v % 4
-  float* tile = (float*)smem;  // TOPK: the 64 x 256 scores, row pitch LPITCH
-  if (TOPK) __syncthreads();   // every wave is done reading the rings
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = i * 32 + (v >> 2) * 8 + khalf * 4 + (v & 3);
-        const int c = wave * 64 + j * 32 + lrow;
-        if (m0 + r < T) logits[(long long)(m0 + r) * E + n0 + c] = acc[i][j][v];
-        if (TOPK) tile[r * LPITCH + c] = acc[i][j][v];
-      }
-  if (!TOPK) return;
-  __syncthreads();
-  // top-k gating of the block's tokens: four per wave at a time, one per
-  // 16-lane row, as in topk_gate16_kernel
-  const int rr = lane & 15;
-  float bl[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) bl[i] = bias ? bias[rr + 16 * i] : 0.0f;
-  for (int r0 = 4 * wave; r0 < BM; r0 += 4 * NW) {
-    const int r = r0 + (lane >> 4);
-    const int t = m0 + r;
-    if (m0 + r0 >= T) break;
-    float sc[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float l = tile[r * LPITCH + rr + 16 * i];
-      sc[i] = bias ? l + bl[i] : l;  // one float32 addition, as in topk_gate_kernel
-    }
-    topk_token16<16>(sc, BN, k, gate, renorm, inv_temp, min_prob, t < T,
-                     topk_idx + (long long)t * k, topk_w + (long long)t * k);
-  }
-}
-
 namespace {
 
 template <int DT>
@@ -602,21 +439,136 @@ int launch_router_mfma(const void* x, const void* wr, int T, int H, int E, float
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+// Router projection for many experts and large batches, paired tiles: a
+// workgroup scores 128 tokens against 128 experts, and the E / 128
+// workgroups that share a token tile run on one XCD at about the same time
+// (block b is XCD b % 8), so the tile's activation rows come from HBM once
+// and from that XCD's L2 for the others.  Against one workgroup per 64
+// tokens x 256 experts this moves 32 KB instead of 40 KB into a compute
+// unit per k-step and keeps the same LDS traffic.  Both operands go through
+// LDS rings of NR 16 KB stages (128-byte rows by global_load_lds,
+// XOR-swizzled chunks; a k-step's A and B copies are issued together); four
+// waves of 64 x 64 (2 x 2 tiles of v_mfma_f32_32x32x16), float32 scores.
 template <int DT>
-int launch_router_ring(const void* x, const void* wr, int T, int H, int E, float* logits,
-                       const float* bias, int k, int gate, int renorm, float inv_temp,
-                       float min_prob, int32_t* idx, float* w, bool topk, hipStream_t s) {
-  // per-lane copy offsets are 32-bit: 256 rows of H values must span < 4 GiB
-  if ((long long)256 * H * 2 >= (1ll << 32)) return MOE_ERR_UNSUPPORTED;
-  const dim3 grid((T + 63) / 64, E / 256);
-  if (topk)
-    hipLaunchKernelGGL((router_ring_kernel<DT, true>), grid, dim3(256), 0, s,
-                       (const uint16_t*)x, (const uint16_t*)wr, T, H, E, logits, bias, k, gate,
-                       renorm, inv_temp, min_prob, idx, w);
-  else
-    hipLaunchKernelGGL((router_ring_kernel<DT, false>), grid, dim3(256), 0, s,
-                       (const uint16_t*)x, (const uint16_t*)wr, T, H, E, logits, bias, k, gate,
-                       renorm, inv_temp, min_prob, idx, w);
+__global__ void __launch_bounds__(256)
+    router_pair_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                       int T, int H, int E, int n_mt, float* __restrict__ logits) {
+  constexpr int BM = 128, BN = 128, ROWB = 128, NW = 4, NR = 4;
+  constexpr int A_STAGE = BM * ROWB, STAGE = (BM + BN) * ROWB;
+  constexpr int JA = BM / 8 / NW, JB = BN / 8 / NW;  // 1 KB copies per wave and stage
+  typedef typename MfmaOp<DT>::V V;
+  __shared__ __attribute__((aligned(1024))) char smem[NR * STAGE];
+  const int nn = E / BN;
+  const int bid = (int)blockIdx.x;
+  const int slot = bid >> 3;
+  const int mt = (slot / nn) * 8 + (bid & 7), nt = slot % nn;
+  if (mt >= n_mt) return;
+  const int tid = (int)threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lrow = lane & 31, khalf = lane >> 5;
+  const int prow = lane >> 3, pchunk = lane & 7;
+  const int sw_row = dma_swz(lrow) ^ khalf;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const char* a_tile = uniform_ptr((const char*)(x + (long long)m0 * H));
+  const char* b_tile = uniform_ptr((const char*)(wr + (long long)n0 * H));
+  // copy j of a wave fills rows 8 (wave + NW j) .. + 7 of its operand (1 KB)
+  uint32_t voffA[JA], voffB[JB];
+#pragma unroll
+  for (int j = 0; j < JA; ++j) {
+    const int row = 8 * (wave + NW * j) + prow;
+    const int grow = min(m0 + row, T - 1);
+    voffA[j] = (uint32_t)(grow - m0) * (uint32_t)(H * 2) + (uint32_t)((pchunk ^ dma_swz(row)) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < JB; ++j) {
+    const int row = 8 * (wave + NW * j) + prow;
+    voffB[j] = (uint32_t)row * (uint32_t)(H * 2) + (uint32_t)((pchunk ^ dma_swz(row)) * 16);
+  }
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  const int nk = H / 64;
+  const uint32_t lds0 = lds_addr(smem);
+#define MOE_ISSUE(st)                                                           \
+  do {                                                                          \
+    const uint32_t dst_ = lds0 + ((st) % NR) * STAGE;                           \
+    _Pragma("unroll") for (int j = 0; j < JA; ++j)                              \
+      dma16(a_tile + (st) * ROWB, voffA[j], dst_ + (wave + NW * j) * 1024);     \
+    _Pragma("unroll") for (int j = 0; j < JB; ++j)                              \
+      dma16(b_tile + (st) * ROWB, voffB[j], dst_ + A_STAGE + (wave + NW * j) * 1024); \
+  } while (0)
+#define MOE_RREAD(As, Bs, s4, FA, FB)                                           \
+  do {                                                                          \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i)                               \
+      FA[i] = *(const V*)((As) + (wm * 64 + i * 32 + lrow) * ROWB + (((2 * (s4)) ^ sw_row) << 4)); \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j)                               \
+      FB[j] = *(const V*)((Bs) + (wn * 64 + j * 32 + lrow) * ROWB +             \
+                          (((2 * (s4)) ^ sw_row) << 4));                        \
+  } while (0)
+#pragma unroll
+  for (int st = 0; st < NR - 1; ++st)
+    if (st < nk) MOE_ISSUE(st);
+  for (int kt = 0; kt < nk; ++kt) {
+    // Stage kt has landed once at most the stages issued after it are in
+    // flight: kt + 1 .. min(kt + NR - 2, nk - 1), JA + JB copies each.  The
+    // barrier then covers every wave's copies and frees the slot read in
+    // iteration kt - 1, which the next issue refills.
+    const int later = min(kt + NR - 2, nk - 1) - kt;
+    if (later >= 2) wait_vmcnt<2 * (JA + JB)>();
+    else if (later == 1) wait_vmcnt<JA + JB>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x7 << 4) | ((0x3F >> 4) << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + NR - 1 < nk) MOE_ISSUE(kt + NR - 1);
+    const char* As = smem + (kt % NR) * STAGE;
+    const char* Bs = As + A_STAGE;
+    V fa0[2], fb0[2], fa1[2], fb1[2];
+    MOE_RREAD(As, Bs, 0, fa0, fb0);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; s4 += 2) {
+      MOE_RREAD(As, Bs, s4 + 1, fa1, fb1);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = MfmaOp<DT>::run(fa0[i], fb0[j], acc[i][j]);
+      if (s4 + 2 < 4) MOE_RREAD(As, Bs, s4 + 2, fa0, fb0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = MfmaOp<DT>::run(fa1[i], fb1[j], acc[i][j]);
+    }
+  }
+#undef MOE_ISSUE
+#undef MOE_RREAD
+  // 32x32 result layout: lane l holds column l % 32, rows 8 * (v / 4) +
+  // 4 * (l / 32) + v % 4
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = m0 + wm * 64 + i * 32 + (v >> 2) * 8 + khalf * 4 + (v & 3);
+        if (r < T) logits[(long long)r * E + n0 + wn * 64 + j * 32 + lrow] = acc[i][j][v];
+      }
+}
+
+template <int DT>
+int launch_router_pair(const void* x, const void* wr, int T, int H, int E, float* logits,
+                       hipStream_t s) {
+  // per-lane copy offsets are 32-bit: 128 rows of H values must span < 4 GiB
+  if ((long long)128 * H * 2 >= (1ll << 32)) return MOE_ERR_UNSUPPORTED;
+  const int n_mt = (T + 127) / 128;
+  const int grid = (n_mt + 7) / 8 * 8 * (E / 128);
+  hipLaunchKernelGGL((router_pair_kernel<DT>), dim3(grid), dim3(256), 0, s,
+                     (const uint16_t*)x, (const uint16_t*)wr, T, H, E, n_mt, logits);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -662,34 +614,10 @@ int route_impl(const void* x, const void* w_router, int act_dtype, const float* 
     // experts, or a small decode batch), or the vector kernel (float32)
     const bool mfma = act_dtype != MOE_DTYPE_F32 && E >= 128 && E % 128 == 0 &&
                       H % 64 == 0 && T >= 1024;
-    if (mfma && E % 256 == 0) {
-      // E == 256: one workgroup holds all of a token's scores, so top-k
-      // gating (k <= 16) runs in the same kernel
-      const bool fuse = E == 256 && k <= 16;
+    if (mfma) {
       st = act_dtype == MOE_DTYPE_F16
-               ? launch_router_ring<MOE_DTYPE_F16>(x, w_router, T, H, E, logits, bias, k, gate,
-                                                   renorm, inv_temp, min_prob, topk_idx,
-                                                   topk_w, fuse, s)
-               : launch_router_ring<MOE_DTYPE_BF16>(x, w_router, T, H, E, logits, bias, k, gate,
-                                                    renorm, inv_temp, min_prob, topk_idx,
-                                                    topk_w, fuse, s);
-      if (st != MOE_OK || fuse) return st;
-    } else if (mfma) {
-      GemmArgs a{};
-      a.A = x;
-      a.lda = H;
-      a.B = w_router;
-      a.strideB = 0;
-      a.ldb = H;
-      a.C = logits;
-      a.ldc = E;
-      a.offsets = nullptr;
-      a.n_groups = 1;
-      a.dense_M = T;
-      a.Nb = E;
-      a.I = 0;
-      a.K = H;
-      st = launch_grouped_gemm(act_dtype, act_dtype, EPI_F32, a, T, s);
+               ? launch_router_pair<MOE_DTYPE_F16>(x, w_router, T, H, E, logits, s)
+               : launch_router_pair<MOE_DTYPE_BF16>(x, w_router, T, H, E, logits, s);
     } else if (act_dtype != MOE_DTYPE_F32 && H % 32 == 0) {
       st = act_dtype == MOE_DTYPE_F16
                ? launch_router_mfma<MOE_DTYPE_F16>(x, w_router, T, H, E, logits, s)

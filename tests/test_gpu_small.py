@@ -106,7 +106,7 @@ ROUTER_SHAPES = [
     small("r_valu_h200", 20, 200, 8, 2, 64, seed_off=73),
     small("r_staged_e256_t1025", 1025, 128, 256, 8, 64, gate=SIGMOID, seed_off=74),
     small("r_staged_e512_f16", 1090, 256, 512, 4, 64, act_dtype=F16, seed_off=75),
-    # E a multiple of 128 but not 256: the grouped GEMM's 64x128 float32 tile
+    # E a multiple of 128 but not 256: three 128-expert tiles per token tile
     small("r_gemm_e384_t1030", 1030, 256, 384, 8, 64, gate=SIGMOID, seed_off=76),
 ]
 
@@ -131,9 +131,9 @@ def test_router_projection_paths(cfg):
 
 
 def test_router_logits_off_alignment():
-    """Logits written to a buffer 4 bytes off 16-byte alignment take the GEMM
-    tile's per-value store path instead of its 16-byte row stores: the same
-    logits, bit for bit, and the same top-k."""
+    """Logits written to a buffer 4 bytes off 16-byte alignment (the
+    projection stores single floats, so any 4-byte alignment serves): the
+    same logits, bit for bit, and the same top-k."""
     from combine_moe_route_02_amd import MoELayer, _lib as L
     cfg = ROUTER_SHAPES[-1]
     inp = to_device(make_inputs(cfg, "cpu", with_weights=False))
