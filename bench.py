@@ -440,8 +440,11 @@ def main():
         small_m = lay.spec.max_rows / n_loc <= 48
         kname = ("grouped_gemm_fp8s" if small_m else "grouped_gemm_mfma") + \
             " (GEMM-1 + SwiGLU, fp8 weights, moe_expert_ffn_up)"
+    elif cfg.act_dtype == "f32":
+        kname = f"grouped_gemm_f32 (GEMM-1 + {cfg.act.upper()}, moe_expert_ffn_up)"
     else:
-        kname = "grouped_gemm_dma (GEMM-1 + SwiGLU, moe_expert_ffn_up)"
+        kname = f"grouped_gemm_dma (GEMM-1 + {'SwiGLU' if cfg.act == 'swiglu' else 'GELU'}, " \
+                "moe_expert_ffn_up)"
     if NB > 1:
         kname += f", one launch per micro-batch of {T // NB} tokens"
     roof["kernel"] = kname
