@@ -412,6 +412,18 @@ def main():
     flops1 = 2.0 * rows_loc * H * 2 * I
     flops2 = 2.0 * rows_loc * I * H
     gemm_tflops = (flops1 + flops2) / ((stage_ms["ffn_up"] + stage_ms["ffn_down"]) * 1e9)
+    # layer roofline: each stage at the larger of its bytes over 8 TB/s and its
+    # flops over the 16-bit matrix peak, summed over the stages
+    wbytes = wb1 + (touched * H * I * (1 if cfg.w_dtype == "e4m3" else w13.element_size()))
+    route_bytes = T * H * ab + E * H * ab + T * E * 4 * 2 + T * k * 8
+    ffn_bytes = wbytes + rows_loc * (H * ab + 2 * I * ab + H * ab)
+    stage_roof_ms = {
+        "route": max(route_bytes / (PEAK_HBM_GBPS * 1e6), 2.0 * T * H * E / (PEAK_MFMA_TFLOPS * 1e9)),
+        "dispatch": disp_bytes / (PEAK_HBM_GBPS * 1e6),
+        "ffn": max(ffn_bytes / (PEAK_HBM_GBPS * 1e6), (flops1 + flops2) / (PEAK_MFMA_TFLOPS * 1e9)),
+        "combine": comb_bytes / (PEAK_HBM_GBPS * 1e6),
+    }
+    layer_roof_ms = sum(stage_roof_ms.values())
     if args.fused:
         flops1 += flops2   # the fused kernel runs both GEMMs (and combine)
     if NB > 1:
@@ -487,6 +499,11 @@ def main():
         "dispatch_combine_frac_hbm": round(dc_gbps / PEAK_HBM_GBPS, 4),
         "gemm_TFLOPs": round(gemm_tflops, 1),
         "gemm_frac_mfma": round(gemm_tflops / PEAK_MFMA_TFLOPS, 4),
+        "layer_roofline": {"ms": round(layer_roof_ms, 5),
+                           "tokens_per_s": round(T / layer_roof_ms * 1e3, 1),
+                           "frac": round(layer_roof_ms / ms_per_step, 4),
+                           "stages_ms": {n: round(v, 5) for n, v in stage_roof_ms.items()}},
+        "tokens_per_s_without_route": round(T / max(ms_per_step - stage_ms["route"], 1e-9) * 1e3, 1),
         "source_hash": source_hash(),
     }
     if not args.no_cpu_baseline:
