@@ -11,10 +11,12 @@ libmoe.so on one HIP stream, inputs already resident in HBM.
 Defaults: the DeepSeek-V3-like EP share (c4, the largest single-GPU layer),
 10 warm-up steps, then 50 timed steps, each bracketed by its own HIP events;
 the line reports their median.  The decode layer (c5) is timed as replays of
-one captured hipGraph, and the small layers (c1, c5) read a 512 MiB buffer
-between steps so that their inputs come from HBM, not the MALL.  The flush
+one captured hipGraph, and the tiny layer (c1) reads a 512 MiB buffer
+between steps so that its inputs come from HBM, not the MALL.  The flush
 reads rather than writes: a written buffer leaves the MALL full of dirty
-lines whose write-back then competes with the next step's reads.
+lines whose write-back then competes with the next step's reads.  The
+decode layer needs none: each step streams 1.4 GB of expert weights, 5.5
+times the MALL, in the same order, so nothing survives to the next step.
 
 Prints one JSON line: whole-layer tokens/s, plus the dominant kernel's
 roofline (GEMM-1, timed live with HIP events on the launch stream), the
@@ -96,7 +98,8 @@ def parse():
     ap.add_argument("--flush", choices=["on", "off", "auto"], default="auto",
                     help="read a 512 MiB buffer between timed steps (outside each "
                          "step's events) so that inputs do not stay in the 256 MiB "
-                         "MALL; auto: on for the small layers c1 and c5")
+                         "MALL; auto: on for the tiny layer c1 (the decode layer's own "
+                         "1.4 GB weight stream evicts everything between its steps)")
     ap.add_argument("--fp8-dispatch", action="store_true",
                     help="send the dispatched rows as E4M3 codes with a per-row scale "
                          "into an fp8 x fp8 GEMM-1 (fp8-weight workloads)")
@@ -273,7 +276,10 @@ def main():
 
     use_graph = args.graph == "on" or (args.graph == "auto" and cfg.name == "c5"
                                        and NB <= 1 and not args.fused and R == 0)
-    flush = args.flush == "on" or (args.flush == "auto" and cfg.name in ("c1", "c5"))
+    # c1 fits in the MALL whole; the decode layer (c5) streams 1.4 GB of expert
+    # weights per step, 5.5x the MALL, so nothing a step reads is still there
+    # when the next one starts and a flush would only add its own write-back
+    flush = args.flush == "on" or (args.flush == "auto" and cfg.name == "c1")
     flush_buf = (torch.ones(64 << 20, dtype=torch.int64, device=dev) if flush else None)
 
     if args.calib_copy_mib:

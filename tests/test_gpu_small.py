@@ -108,6 +108,9 @@ ROUTER_SHAPES = [
     small("r_staged_e512_f16", 1090, 256, 512, 4, 64, act_dtype=F16, seed_off=75),
     # E a multiple of 128 but not 256: three 128-expert tiles per token tile
     small("r_gemm_e384_t1030", 1030, 256, 384, 8, 64, gate=SIGMOID, seed_off=76),
+    # one expert tile per token tile; a single k-step, and two
+    small("r_pair_e128_h64", 1100, 64, 128, 4, 64, seed_off=77),
+    small("r_pair_e256_h128_t2049", 2049, 128, 256, 8, 64, gate=SIGMOID, seed_off=78),
 ]
 
 
