@@ -533,18 +533,25 @@ do {                                                                            
     _Pragma("unroll") for (int j = 0; j < TN; ++j)                                 \
       acc[i][j] = MO::run(FA[i], FB[j], acc[i][j]);                                \
 } while (0)
-// Fragment read r (r < TM: A block r, else B block r - TM) of substep s4
-// of a stage, and the MFMA after which it is issued: the TM + TN reads are
-// spread evenly over the TM * TN MFMAs of a substep.
+// Fragment read r of substep s4 of a stage, and the MFMA after which it is
+// issued: the TM + TN reads are spread evenly over the TM * TN MFMAs of a
+// substep.  MOE_FRAG(r) < TM is A block MOE_FRAG(r), else B block
+// MOE_FRAG(r) - TM.  The next substep's MFMAs run A block 0 against every B
+// block first, then A blocks 1 .. TM - 1, so the reads follow that order:
+// each read then has at least a third of a substep of MFMAs before its
+// first use (read in A-then-B order, the last B block had eight MFMAs; 0.5-1%
+// faster per GEMM measured, same sums).
+#define MOE_FRAG(r) ((r) == 0 ? 0 : (r) <= TN ? TM + (r) - 1 : (r) - TN)
 #define MOE_READ1(stage, s4, r, NA, NB)                                            \
 do {                                                                             \
     const char* As_ = smem + (stage) * STAGE;                                      \
     const char* Bs_ = As_ + A_BYTES;                                               \
-    if ((r) < TM)                                                                  \
-      NA[r] = *(const V*)(As_ + (wm * WTM + (r) * MI + lrow) * ROWB + ((((KSUB / 8) * (s4)) ^ sw_row) << 4)); \
+    const int f_ = MOE_FRAG(r);                                                    \
+    if (f_ < TM)                                                                   \
+      NA[f_] = *(const V*)(As_ + (wm * WTM + f_ * MI + lrow) * ROWB + ((((KSUB / 8) * (s4)) ^ sw_row) << 4)); \
     else                                                                           \
-      NB[(r) - TM] = *(const V*)(Bs_ + (wn * WTN + ((r) - TM) * MI + lrow) * ROWB +       \
-                                 ((((KSUB / 8) * (s4)) ^ sw_row) << 4));           \
+      NB[f_ - TM] = *(const V*)(Bs_ + (wn * WTN + (f_ - TM) * MI + lrow) * ROWB +         \
+                                ((((KSUB / 8) * (s4)) ^ sw_row) << 4));            \
 } while (0)
 #define MOE_READ_AT(r) (((r) + 1) * (TM * TN) / (TM + TN) > 0 ? ((r) + 1) * (TM * TN) / (TM + TN) - 1 : 0)
 // The MFMAs of one substep (operands FA, FB) with the fragment reads of
@@ -689,6 +696,7 @@ do {                                                                            
 #undef MOE_READ
 #undef MOE_MFMAS_READ
 #undef MOE_READ1
+#undef MOE_FRAG
 #undef MOE_READ_AT
 #undef MOE_MFMAS
 #undef MOE_STAGE_READY
