@@ -34,6 +34,36 @@ __device__ __forceinline__ float key_score(uint64_t key) {
   return __uint_as_float(b);
 }
 
+// Max and sum over the 16 lanes of this lane's DPP row (lanes 16 r .. 16 r +
+// 15), every lane receiving the result: four row rotations by 1, 2, 4 and 8
+// lanes (v_mov_b32_dpp row_ror), no LDS permute.  The max is exact; the sum's
+// association depends on the lane, so lanes may differ in the last bit.
+__device__ __forceinline__ uint64_t row16_max_u64(uint64_t v) {
+#define MOE_ROW_MAX(CTRL)                                                                  \
+  do {                                                                                     \
+    const uint32_t lo_ = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xf,  \
+                                                            0xf, false);                  \
+    const uint32_t hi_ = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, \
+                                                            0xf, 0xf, false);             \
+    const uint64_t w_ = ((uint64_t)hi_ << 32) | lo_;                                       \
+    v = w_ > v ? w_ : v;                                                                   \
+  } while (0)
+  MOE_ROW_MAX(0x121);
+  MOE_ROW_MAX(0x122);
+  MOE_ROW_MAX(0x124);
+  MOE_ROW_MAX(0x128);
+#undef MOE_ROW_MAX
+  return v;
+}
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x121, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x122, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
+  return v;
+}
+
 // Top-k gating of one token by one wave: lane l holds the scores s[i] (bias
 // added) of experts e = l + 64 i, i < EPL (experts past E must not count).
 // k rounds of a wave-wide uint64 max pick the experts in descending order;
@@ -65,12 +95,39 @@ __device__ __forceinline__ void topk_token(const float (&s)[EPL], int E, int k, 
   const float smax = key_score(top);
   float w = 0.0f;
   const float sj = key_score(mine);
+  // With k <= 16 the two sums are taken in the order of the 16-lane
+  // selection (topk_token16): lane r < 16 adds the terms of experts r + 16 i
+  // in i order, then the lanes 0..15 combine by the same row rotations, so a
+  // token gets the same weights, bit for bit, from either kernel (which one
+  // runs depends on the batch size).  Expert r + 16 i is held by lane
+  // r + 16 (i % 4), slot i / 4.
+  const bool rows16 = k <= 16;
   if (gate == MOE_GATE_SOFTMAX) {
-    float part = 0.0f;
+    float x[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
-      if (lane + 64 * i < E) part += expf((s[i] - smax) * inv_temp);
-    const float denom = wave_sum(part);
+      x[i] = lane + 64 * i < E ? expf((s[i] - smax) * inv_temp) : 0.0f;
+    float denom;
+    if (rows16) {
+      float y[3][EPL];
+#pragma unroll
+      for (int q = 1; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) y[q - 1][i] = __shfl(x[i], (lane + 16 * q) & 63, MOE_WAVE);
+      float part = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4 * EPL; ++i) {
+        const int q = i & 3, slot = i >> 2;
+        if ((lane & 15) + 16 * i < E) part += q == 0 ? x[slot] : y[q - 1][slot];
+      }
+      denom = row16_sum(part);
+    } else {
+      float part = 0.0f;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane + 64 * i < E) part += x[i];
+      denom = wave_sum(part);
+    }
     w = expf((sj - smax) * inv_temp) / denom;
   } else {
     w = 1.0f / (1.0f + expf(-sj));
@@ -79,43 +136,13 @@ __device__ __forceinline__ void topk_token(const float (&s)[EPL], int E, int k, 
   const bool keep = !(min_prob > 0.0f) || w > min_prob;
   if (!keep) w = 0.0f;
   if (renorm) {
-    const float tot = wave_sum(lane < k ? w : 0.0f);
+    const float tot = rows16 ? row16_sum(lane < k ? w : 0.0f) : wave_sum(lane < k ? w : 0.0f);
     w = tot > 0.0f ? w / tot : 0.0f;
   }
   if (lane < k) {
     idx_row[lane] = keep ? (int32_t)(~(uint32_t)mine) : -1;
     w_row[lane] = w;
   }
-}
-
-// Max and sum over the 16 lanes of this lane's DPP row (lanes 16 r .. 16 r +
-// 15), every lane receiving the result: four row rotations by 1, 2, 4 and 8
-// lanes (v_mov_b32_dpp row_ror), no LDS permute.  The max is exact; the sum's
-// association depends on the lane, so lanes may differ in the last bit.
-__device__ __forceinline__ uint64_t row16_max_u64(uint64_t v) {
-#define MOE_ROW_MAX(CTRL)                                                                  \
-  do {                                                                                     \
-    const uint32_t lo_ = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xf,  \
-                                                            0xf, false);                  \
-    const uint32_t hi_ = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, \
-                                                            0xf, 0xf, false);             \
-    const uint64_t w_ = ((uint64_t)hi_ << 32) | lo_;                                       \
-    v = w_ > v ? w_ : v;                                                                   \
-  } while (0)
-  MOE_ROW_MAX(0x121);
-  MOE_ROW_MAX(0x122);
-  MOE_ROW_MAX(0x124);
-  MOE_ROW_MAX(0x128);
-#undef MOE_ROW_MAX
-  return v;
-}
-
-__device__ __forceinline__ float row16_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x121, 0xf, 0xf, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x122, 0xf, 0xf, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xf, 0xf, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
-  return v;
 }
 
 // Top-k gating of four tokens at once, one 16-lane row of the wave each:
@@ -575,7 +602,14 @@ int launch_router_pair(const void* x, const void* wr, int T, int H, int E, float
 int launch_topk(const float* logits, const float* bias, int T, int E, int k,
                 int gate, int renorm, float inv_temp, float min_prob, int32_t* idx,
                 float* w, hipStream_t s) {
-  if (E <= 256 && k <= 16) {
+  // Sixteen lanes per token pay off once there are enough tokens to fill the
+  // chip; below that the selection's dependency chain is the latency, and a
+  // wave per token (a quarter of the experts per lane) is shorter: route
+  // step 32 -> 26 us at 128 tokens x 256 experts, 3-6 us less up to 4096
+  // tokens, 2-12 us more from 8192 (256 experts; with 128 or fewer experts
+  // the wave kernel is ahead only up to about 256 tokens).
+  const bool wide = E > 128 ? T > 4096 : T > 512;
+  if (E <= 256 && k <= 16 && wide) {
     // four tokens per wave, sixteen per block
     const dim3 grid16((T + 15) / 16), block16(256);
 #define MOE_TOPK16(EPL)                                                              \

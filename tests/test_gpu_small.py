@@ -185,16 +185,19 @@ def test_empty_input():
     assert lay.offsets.cpu().tolist() == [0] * 9
 
 
-def test_mass_ties_in_scores():
-    """Scores in {-1, -0, +0, 1}: selection must follow (score desc, index asc)."""
+@pytest.mark.parametrize("T", [500, 4100])
+def test_mass_ties_in_scores(T):
+    """Scores in {-1, -0, +0, 1}: selection must follow (score desc, index asc).
+    500 tokens take the wave-per-token selection, 4100 the 16-lane one
+    (E <= 256)."""
     from combine_moe_route_02_amd import MoELayer
     for E, k in [(16, 4), (256, 8), (8, 8), (1024, 32)]:
-        cfg = small(f"ties_{E}", 500, 256, E, k, 128, seed_off=30 + E)
+        cfg = small(f"ties_{E}", T, 256, E, k, 128, seed_off=30 + E)
         lay = MoELayer(spec(cfg), "cuda")
         g = torch.Generator().manual_seed(E)
-        s = torch.randint(-1, 2, (500, E), generator=g).float()
-        s[torch.rand((500, E), generator=g) < 0.2] = -0.0
-        say(f"[gpu] route ties E={E} k={k}")
+        s = torch.randint(-1, 2, (T, E), generator=g).float()
+        s[torch.rand((T, E), generator=g) < 0.2] = -0.0
+        say(f"[gpu] route ties T={T} E={E} k={k}")
         lay.logits.copy_(s.cuda())
         lay.route_from_logits()
         torch.cuda.synchronize()
@@ -210,23 +213,53 @@ GATE_CASES = [("softmax", False, 1 / 0.3, 0.0), ("softmax", True, 1.0, 0.0),
               ("sigmoid", True, 1.0, 0.93), ("sigmoid", False, 1.0, 0.985)]
 
 
-def test_gate_variants_on_given_scores():
-    """Temperature, sigmoid and renormalisation on the same scores."""
+@pytest.mark.parametrize("T", [300, 600])
+def test_gate_variants_on_given_scores(T):
+    """Temperature, sigmoid and renormalisation on the same scores (300
+    tokens: wave-per-token selection; 600, the same 300 rows twice: the
+    16-lane one).  The scores keep every gate value well away from the
+    thresholds, so the kept sets are unique."""
     from combine_moe_route_02_amd import MoELayer
     g = torch.Generator().manual_seed(5)
     s = torch.randn((300, 64), generator=g) * 2
     bias = torch.randn(64, generator=g)
+    s = s.repeat(T // 300, 1)
     for gate, renorm, invt, thr in GATE_CASES:
-        cfg = small("gates", 300, 256, 64, 6, 128, gate=gate, renorm=renorm,
+        cfg = small("gates", T, 256, 64, 6, 128, gate=gate, renorm=renorm,
                     inv_t=invt, min_prob=thr)
         lay = MoELayer(spec(cfg), "cuda")
         lay.logits.copy_(s.cuda())
-        say(f"[gpu] route gate={gate} renorm={renorm} inv_t={invt} min_prob={thr}")
+        say(f"[gpu] route T={T} gate={gate} renorm={renorm} inv_t={invt} min_prob={thr}")
         lay.route_from_logits(bias.cuda())
         torch.cuda.synchronize()
         idx, w = route(cfg, s.numpy(), bias.numpy())
         assert np.array_equal(lay.topk_idx.cpu().numpy(), idx)
         assert rel_l2(lay.topk_w.cpu().numpy(), w) <= TOL_F32
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (64, 6), (128, 8), (256, 8), (256, 16)])
+def test_topk_paths_agree_bitwise(E, k):
+    """The 16-lane selection (large batches) and the wave-per-token one
+    (small batches) return the same picks and the same weight bits for the
+    same scores, so a token's routing does not depend on its batch size."""
+    from combine_moe_route_02_amd import MoELayer
+    T_big, T_small = 4100, 500
+    g = torch.Generator().manual_seed(E + k)
+    s = torch.randn((T_big, E), generator=g) * 2
+    bias = torch.randn(E, generator=g)
+    for gate, renorm, invt, thr in GATE_CASES:
+        out = []
+        for T in (T_big, T_small):
+            cfg = small("paths", T, 256, E, k, 128, gate=gate, renorm=renorm,
+                        inv_t=invt, min_prob=thr)
+            lay = MoELayer(spec(cfg), "cuda")
+            lay.logits.copy_(s[:T].cuda())
+            say(f"[gpu] route paths T={T} E={E} k={k} gate={gate} renorm={renorm}")
+            lay.route_from_logits(bias.cuda())
+            torch.cuda.synchronize()
+            out.append((lay.topk_idx.cpu(), lay.topk_w.cpu()))
+        assert torch.equal(out[0][0][:T_small], out[1][0])
+        assert torch.equal(out[0][1][:T_small], out[1][1])
 
 
 def test_repeat_runs_are_bitwise_identical():
