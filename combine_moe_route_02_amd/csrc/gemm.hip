@@ -276,18 +276,21 @@ __global__ void __launch_bounds__(WM * WN * 64)
 // fp32 partial sums.  Four waves, each 32 x 64 (two 32x32 MFMA columns).
 // ---------------------------------------------------------------------------
 
-// 8 E4M3 codes -> 8 bf16, exact (every E4M3 value is a bf16 value, so the
-// low 16 bits of the decoded f32 are zero).
+// 8 E4M3 codes -> 8 bf16, exact (every E4M3 value is a bf16 value): one
+// v_cvt_scalef32_pk_bf16_fp8 per two codes, with scale 1 (through f32 with
+// v_cvt_pk_f32_fp8 it takes three instructions per two codes; same bits for
+// all 256 codes).
 __device__ __forceinline__ bf16x8 decode_fp8x8(uint32_t lo, uint32_t hi) {
-  const uint32_t w[2] = {lo, hi};
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);  // bytes 0, 1
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);   // bytes 2, 3
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
   u32x4 u;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);  // bytes 0, 1
-    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);   // bytes 2, 3
-    u[2 * i] = (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xffff0000u);
-    u[2 * i + 1] = (__float_as_uint(b[0]) >> 16) | (__float_as_uint(b[1]) & 0xffff0000u);
-  }
+  u[0] = __builtin_bit_cast(uint32_t, a);
+  u[1] = __builtin_bit_cast(uint32_t, b);
+  u[2] = __builtin_bit_cast(uint32_t, c);
+  u[3] = __builtin_bit_cast(uint32_t, d);
   return __builtin_bit_cast(bf16x8, u);
 }
 
@@ -316,6 +319,7 @@ struct Fp8SmallTile {
   static constexpr int BPW = (A_BLK + B_BLK) / NW;
   static constexpr int JA = A_BLK / NW;
   static constexpr int SMEM = NS * STAGE;
+  static constexpr int SR = 4;  // scale registers per column group: K <= 64 * SR * BK
   static_assert(A_BLK % NW == 0 && B_BLK % NW == 0 && 2 * BPW < 64, "blocks");
 
   __device__ static __forceinline__ void run(const GemmArgs& p, const TileInfo& ti, int nt,
@@ -384,7 +388,6 @@ struct Fp8SmallTile {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][v] = 0.0f;
 
-    const int nk = p.K / BK;
     const uint32_t lds0 = lds_addr(smem);
 #define MOE_ISSUE8(st)                                                             \
 do {                                                                             \
@@ -397,6 +400,22 @@ do {                                                                            
     }                                                                            \
 } while (0)
 
+    // The k-step scales of this wave's column groups, lane l holding k-step
+    // l + 64 q in register q; read per k-step with v_readlane.  Loaded and
+    // waited for here, before any copy is in flight: a vector load of the
+    // scale inside the k-loop would make the wait for it (vmcnt counts in
+    // issue order) also wait for the two stages of copies issued before it,
+    // draining the copy pipeline every k-step.
+    const int nk = p.K / BK;
+    float scr[TN][SR];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < SR; ++q) {
+        const int kk = lane + 64 * q;
+        scr[j][q] = kk < nk ? srow[j][kk] : 0.0f;
+      }
+    wait_vmcnt<0>();
     lds_barrier();  // every wave is done with the previous tile's stages
     MOE_ISSUE8(0);
     if (nk > 1) MOE_ISSUE8(1);
@@ -410,7 +429,13 @@ do {                                                                            
       if (kt + 2 < nk) MOE_ISSUE8(kt + 2);
       float sc[TN];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) sc[j] = srow[j][kt];
+      for (int j = 0; j < TN; ++j) {
+        float r = scr[j][0];
+#pragma unroll
+        for (int q = 1; q < SR; ++q)
+          if ((kt >> 6) == q) r = scr[j][q];
+        sc[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r), kt & 63));
+      }
       const char* As = smem + (kt % NS) * STAGE;
       const char* Bs = As + A_BYTES;
       f32x16 part[TN];
@@ -756,7 +781,8 @@ int launch_fp8s(GemmArgs a, int max_rows, hipStream_t s) {
 // each (SwiGLU keeps 256: a wave pairs gate and up columns).
 template <int DT, int EPI, bool A8 = false>
 int run_fp8s(GemmArgs a, int max_rows, hipStream_t s) {
-  if (a.Nb % 256 || a.K % 128) return MOE_ERR_UNSUPPORTED;
+  // K: whole 128-wide scale blocks, at most 64 * SR of them in the scale registers
+  if (a.Nb % 256 || a.K % 128 || a.K > 64 * 4 * 128) return MOE_ERR_UNSUPPORTED;
   if ((long long)a.Nb * a.ldb >= (1ll << 32)) return MOE_ERR_UNSUPPORTED;
   if (a.offsets && a.n_groups > 1024) return MOE_ERR_UNSUPPORTED;
   if constexpr (EPI != EPI_SWIGLU) {
@@ -825,7 +851,10 @@ inline bool few_rows(const GemmArgs& a, int max_rows) {
 template <int DT, int WK, int EPI>
 int pick_tile(GemmArgs a, int max_rows, hipStream_t s) {
   if (few_rows(a, max_rows)) {
-    if constexpr (WK == W_FP8 && DT == MOE_DTYPE_BF16) return run_fp8s<DT, EPI>(a, max_rows, s);
+    if constexpr (WK == W_FP8 && DT == MOE_DTYPE_BF16) {
+      const int st = run_fp8s<DT, EPI>(a, max_rows, s);
+      if (st != MOE_ERR_UNSUPPORTED) return st;  // else the register-staged tile below
+    }
     return run_mfma<DT, WK, EPI, 32, 256, 1, 4>(a, max_rows, 1, s);
   }
   if constexpr (WK == W_SAME) {

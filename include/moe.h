@@ -193,8 +193,9 @@ int moe_dispatch_fp8(const void* x, int act_dtype, const int32_t* topk_idx,
  *  w13, w13_scale     E4M3 weights and their 128x128 block scales, as for
  *                     moe_expert_ffn with w_dtype MOE_DTYPE_FP8_E4M3.
  *  h_ws               [max_rows][I] bf16 output, row r - offsets[e_begin].
- * Limits: H % 128 == 0, I % 128 == 0 (MOE_ERR_UNSUPPORTED otherwise).  The
- * 32-row tile serves every row count (it is built for decode batches).
+ * Limits: H % 128 == 0, H <= 32768, I % 128 == 0 (MOE_ERR_UNSUPPORTED
+ * otherwise).  The 32-row tile serves every row count (it is built for
+ * decode batches).
  * GEMM-2 and combine are moe_expert_ffn_down and moe_combine, unchanged.
  */
 int moe_expert_ffn_up_fp8(const void* x_perm_q, const float* x_scale,
