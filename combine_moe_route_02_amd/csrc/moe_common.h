@@ -105,11 +105,25 @@ template <> struct Act<MOE_DTYPE_F16> {
   typedef uint16_t T;
   static __device__ __forceinline__ float load(T v) { return f16_to_f32(v); }
   static __device__ __forceinline__ T store(float f) { return f32_to_f16(f); }
+  // two values, a in the low half
+  static __device__ __forceinline__ uint32_t store2(float a, float b) {
+    return (uint32_t)f32_to_f16(a) | ((uint32_t)f32_to_f16(b) << 16);
+  }
 };
 template <> struct Act<MOE_DTYPE_BF16> {
   typedef uint16_t T;
   static __device__ __forceinline__ float load(T v) { return bf16_to_f32(v); }
   static __device__ __forceinline__ T store(float f) { return f32_to_bf16(f); }
+  // two values in one packed conversion (v_cvt_pk_bf16_f32), a in the low half
+  static __device__ __forceinline__ uint32_t store2(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const f2 v = {a, b};
+    const b2 h = __builtin_convertvector(v, b2);
+    uint32_t r;
+    __builtin_memcpy(&r, &h, 4);
+    return r;
+  }
 };
 
 // 16 bytes of a 16-bit activation row -> 8 floats.
