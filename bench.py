@@ -740,7 +740,8 @@ def stats_summary(stats_csv, out_path, workload="c2", extra=""):
     # per-dispatch durations of this library's kernels from the kernel trace
     # written beside the stats: the median (the first launches of a process
     # include cold caches and page mapping)
-    trace = stats_csv.replace("kernel_stats", "kernel_trace")
+    trace = os.path.join(os.path.dirname(stats_csv),
+                         os.path.basename(stats_csv).replace("kernel_stats", "kernel_trace"))
     if trace != stats_csv and os.path.exists(trace):
         import statistics
         per = {}
