@@ -344,3 +344,48 @@ def test_dispatch_layout_paths(T, E, k):
     st = {"x": stored(x), "bias": bias.numpy()}
     r = check_routing(cfg, lay, st)
     assert int(r["offsets"][-1]) == T * k
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+def test_combine_rounds_like_torch(dt):
+    """The float32 -> 16-bit rounding of the library's stores (here through
+    combine with k = 1: out = w * y, rounded once to float32, then to the row
+    type) against torch's own conversion of the same float32 product, bit for
+    bit.  Inputs cover normal and subnormal 16-bit values and values near the
+    format's maximum; weights give exact ties (1 + 2^-8 for bf16, 1 + 2^-11
+    for f16), underflow into subnormal results and overflow to infinity.
+    Only the sign of a zero result may differ (the kernel accumulates onto
+    +0)."""
+    from combine_moe_route_02_amd import _lib as L
+    T, H = 2048, 256
+    g = np.random.default_rng(BASE_SEED + 71)
+    bits = g.integers(0, 1 << 16, size=(T, H), dtype=np.uint32)
+    emax = 0x7F80 if dt == torch.bfloat16 else 0x7C00   # exponent all ones: inf/NaN
+    sign = bits & 0x8000
+    mag = bits & 0x7FFF
+    mag = np.where(mag >= emax, mag - emax, mag)            # no inf or NaN inputs
+    # a quarter of the rows subnormal (exponent field 0), a few near the maximum
+    sub_mask = 0x007F if dt == torch.bfloat16 else 0x03FF
+    rows = np.arange(T)[:, None]
+    mag = np.where(rows % 4 == 1, mag & sub_mask, mag)
+    mag = np.where(rows % 16 == 2, emax - 1 - (mag & 0xFF), mag)
+    y16 = torch.from_numpy((sign | mag).astype(np.int32)).to(torch.int16).view(dt)
+    tie = 1.0 + (2.0 ** -8 if dt == torch.bfloat16 else 2.0 ** -11)
+    choices = np.array([1.0, tie, 1.0 - 2.0 ** -9, 3.0, 2.0 ** -20, 0.7], dtype=np.float32)
+    w = choices[np.arange(T) % len(choices)]
+    w = np.where(np.arange(T) % 7 == 6, g.uniform(-4, 4, size=T).astype(np.float32), w)
+    y = y16.cuda()
+    wt = torch.from_numpy(w.astype(np.float32)).cuda()
+    slot = torch.arange(T, dtype=torch.int32, device="cuda").view(T, 1)
+    out = torch.empty((T, H), dtype=dt, device="cuda")
+    L.moe_combine(y, slot, wt.view(T, 1), out)
+    torch.cuda.synchronize()
+    ref = (y.float() * wt[:, None]).to(dt)
+    a = out.view(torch.int16).int() & 0xFFFF
+    b = ref.view(torch.int16).int() & 0xFFFF
+    zero = ((a & 0x7FFF) == 0) & ((b & 0x7FFF) == 0)
+    bad = (a != b) & ~zero
+    say(f"  {dt}: {int(bad.sum())} of {T * H} outputs differ; "
+        f"{int(torch.isinf(ref.float()).sum())} infinities, "
+        f"{int(((b & emax) == 0).sum())} subnormal or zero results")
+    assert int(bad.sum()) == 0
