@@ -292,11 +292,16 @@ __device__ __forceinline__ void lds_barrier() {
 // address registers).  Issued from asm so that the compiler does not add its
 // own conservative vmcnt(0) before every later LDS read; the instruction
 // writes no VGPR, and the kernel's counted vmcnt waits order it before the
-// reads of its stage.
+// reads of its stage.  The LDS address goes in M0 as an asm operand, so the
+// compiler sets M0 itself: a wave's copies into one stage lie a constant
+// apart, and each costs one scalar add to M0 from the stage's base register
+// (setting M0 inside the asm from a precomputed register per copy took twice
+// the scalar instructions and the registers spilled to vector lanes; c4
+// GEMM-1 and GEMM-2 ran 2-5% slower).
 __device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("global_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(base), "s"(lds_base)
+               : "v"(voff), "s"(base), "{m0}"(lds_base)
                : "memory");
 }
 
@@ -304,9 +309,9 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t 
 // batch's fp8 weights: each weight line serves one tile).
 __device__ __forceinline__ void dma16_stream(const char* base, uint32_t voff,
                                              uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+  asm volatile("global_load_lds_dwordx4 %0, %1 nt"
                :
-               : "v"(voff), "s"(base), "s"(lds_base)
+               : "v"(voff), "s"(base), "{m0}"(lds_base)
                : "memory");
 }
 
@@ -314,9 +319,9 @@ __device__ __forceinline__ void dma16_stream(const char* base, uint32_t voff,
 // slot that nothing reads (lane l writes lds_base + 4 * l), which brings the
 // lines into L2 ahead of their stage's copy.  Counted by vmcnt like dma16.
 __device__ __forceinline__ void prefetch4(const char* base, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+  asm volatile("global_load_lds_dword %0, %1"
                :
-               : "v"(voff), "s"(base), "s"(lds_base)
+               : "v"(voff), "s"(base), "{m0}"(lds_base)
                : "memory");
 }
 
@@ -386,6 +391,7 @@ struct DmaTile {
   static_assert(EPI != EPI_SWIGLU || (TN % (MI == 32 ? 2 : 4)) == 0, "swiglu pairs");
   static_assert(PFD >= 3 && BPW + (PFD - 2) * NPF < 64, "vmcnt range");
   static_assert(MI == 32 || MI == 16, "MFMA shape");
+  static_assert(A_BYTES == A_BLK * 1024, "B blocks start right after the A blocks");
 
   static constexpr int NACC = TM * TN * NV;  // accumulators per thread
   static constexpr long long SLOT = (long long)NT * NACC;  // floats per split slot
@@ -477,7 +483,7 @@ struct DmaTile {
           n = n0 + row;
         }
         voff[j] = (uint32_t)n * (uint32_t)(p.ldb * 2) + (uint32_t)(kc * 16);
-        ldsoff[j] = A_BYTES + (q - A_BLK) * 1024;
+        ldsoff[j] = q * 1024;  // the B blocks follow the A_BLK blocks of A
       }
     }
 
